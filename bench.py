@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 delayed-scaling Linear on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the fwd+bwd Linear at 4096 hidden with M = 16384 tokens (X, W, dY bf16; HYBRID
+recipe E4M3 forward / E5M2 gradients; amax history 16, window max, margin 0):
+
+  cast X, cast W (fused amax)  ->  Y = Xq Wq (NN)  ->  cast dY  ->
+  dX = dYq Wq^T (NT)  ->  dW = Xq^T dYq (TN)  ->  scale update of 3 histories
+
+`value` is the step's FP8 GEMM work (3 x 2 M N K flop) divided by the measured
+time of the whole step (casts and scale update included), in TFLOP/s.  Inputs
+are resident in HBM before timing; four input sets are rotated so that the
+256 MB Infinity Cache cannot hold a step's working set.  Per-kernel times come
+from HIP events recorded on the stream the kernels are launched on.
+
+Prints one JSON line.  `--gpus N` with N > 1 is not supported (single-GPU build).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M_TOK, K_IN, N_OUT = 16384, 4096, 4096
+HIST_LEN = 16
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0    # MI355X HBM3E
+N_SETS = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stress", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(xb, wb, dyb, rows=1024):
+    """The oracle's training step on a row sample of the same workload (CPU)."""
+    from oracle import bf16 as obf16
+    from oracle import fp8 as ofp8
+    from oracle import linear as olinear
+    from oracle.scaling import ScalingState
+
+    states = {"x": ScalingState(ofp8.E4M3, HIST_LEN), "w": ScalingState(ofp8.E4M3, HIST_LEN),
+              "dy": ScalingState(ofp8.E5M2, HIST_LEN)}
+    x = obf16.widen(xb[:rows])
+    w = obf16.widen(wb)
+    dy = obf16.widen(dyb[:rows])
+    t0 = time.perf_counter()
+    olinear.train_step(x, w, dy, states, 0, 0)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2 * rows * K_IN * N_OUT
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"one oracle fwd+bwd step on the first {rows} of {M_TOK} token rows "
+                  f"(casts of X[{rows}x{K_IN}], W[{K_IN}x{N_OUT}], dY[{rows}x{N_OUT}]; three exact "
+                  f"fp64 GEMMs of {rows}x{K_IN}x{N_OUT}); {dt:.2f} s",
+        "seconds": round(dt, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+              "(the multi-GPU design is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import delayed_scaling_gemm_amd as dsg
+    import workloads
+    from delayed_scaling_gemm_amd.linear import DelayedScalingLinear
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating inputs M={M_TOK} K={K_IN} N={N_OUT}", file=sys.stderr, flush=True)
+    xb, wb, dyb = workloads.fwd_bwd_4096(M_TOK, K_IN, N_OUT)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base = [to_dev(xb), to_dev(wb), to_dev(dyb)]
+    sets = [base] + [[t.clone() for t in base] for _ in range(N_SETS - 1)]
+    torch.cuda.synchronize()
+
+    lin = DelayedScalingLinear(hist_len=HIST_LEN, algo=dsg.ALGO_MAX, margin=0, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # the step, with an event after each launch so per-kernel times are measured live
+    names = ["cast_x", "cast_w", "gemm_nn_fwd", "cast_dy", "gemm_nt_dgrad", "gemm_tn_wgrad",
+             "scale_update"]
+
+    def step_with_events(x, w, dy, ev):
+        from delayed_scaling_gemm_amd import (E4M3, E5M2, OP_N, OP_T, fp8ds_cast, fp8ds_gemm,
+                                              fp8ds_scale_update)
+        M, K = x.shape
+        N = w.shape[1]
+        bufs = lin._bufs
+        if "xq" not in bufs:
+            lin.step(x, w, dy)  # allocates the output buffers once
+        xq, wq, y, dyq, dx, dw = (bufs[k] for k in ("xq", "wq", "y", "dyq", "dx", "dw"))
+        s, su, am, sat = lin.scale, lin.scale_used, lin.amax, lin.sat
+        ev[0].record(stream)
+        fp8ds_cast(x, E4M3, s[0:1], xq, None, su[0:1], am[0:1], sat[0:1])
+        ev[1].record(stream)
+        fp8ds_cast(w, E4M3, s[1:2], wq, None, su[1:2], am[1:2], sat[1:2])
+        ev[2].record(stream)
+        fp8ds_gemm(OP_N, OP_N, M, N, K, xq, E4M3, K, su[0:1], wq, E4M3, N, su[1:2], y, N,
+                   lin.amax_y)
+        ev[3].record(stream)
+        fp8ds_cast(dy, E5M2, s[2:3], dyq, None, su[2:3], am[2:3], sat[2:3])
+        ev[4].record(stream)
+        fp8ds_gemm(OP_N, OP_T, M, K, N, dyq, E5M2, N, su[2:3], wq, E4M3, N, su[1:2], dx, K)
+        ev[5].record(stream)
+        fp8ds_gemm(OP_T, OP_N, K, N, M, xq, E4M3, K, su[0:1], dyq, E5M2, N, su[2:3], dw, N)
+        ev[6].record(stream)
+        fp8ds_scale_update(lin.history, lin.cursor, am, lin.fmts, lin.algo, lin.margin, s)
+        ev[7].record(stream)
+
+    for i in range(args.warmup):
+        x, w, dy = sets[i % N_SETS]
+        lin.step(x, w, dy)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        x, w, dy = sets[i % N_SETS]
+        step_with_events(x, w, dy, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+
+    per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(7)]
+                    for i in range(args.steps)])  # ms
+    step_ms = np.array([evs[i][0].elapsed_time(evs[i][7]) for i in range(args.steps)])
+    ms_per_step = float(step_ms.mean())
+    flop_gemm = 2.0 * M_TOK * K_IN * N_OUT
+    value = 3 * flop_gemm / (ms_per_step * 1e-3) / 1e12
+    avg = {n: float(per[:, j].mean()) for j, n in enumerate(names)}
+    gemm_tflops = {n: round(flop_gemm / (avg[n] * 1e-3) / 1e12, 1)
+                   for n in ("gemm_nn_fwd", "gemm_nt_dgrad", "gemm_tn_wgrad")}
+    cast_bytes = {"cast_x": M_TOK * K_IN * 3, "cast_w": K_IN * N_OUT * 3,
+                  "cast_dy": M_TOK * N_OUT * 3}
+    cast_gbps = {n: round(b / (avg[n] * 1e-3) / 1e9, 1) for n, b in cast_bytes.items()}
+    dom = max(gemm_tflops, key=lambda n: avg[n])
+    achieved = flop_gemm / (avg[dom] * 1e-3) / 1e12
+    result = {
+        "metric": "FP8 scaled-GEMM TFLOP/s (% FP8 MFMA peak); amax+cast GB/s (% HBM peak)",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": "fwd+bwd FP8 delayed-scaling Linear, 4096 hidden, M=16384 tokens "
+                        "(X, W, dY bf16; HYBRID E4M3/E5M2; history 16, max, margin 0)",
+            "M": M_TOK, "K": K_IN, "N": N_OUT, "hist_len": HIST_LEN,
+        },
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cast_roofline": {
+            "kernel": "cast_x",
+            "bound": "hbm",
+            "achieved": cast_gbps["cast_x"],
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(cast_gbps["cast_x"] / PEAK_HBM_GBPS, 4),
+        },
+        "gemm_tflops": gemm_tflops,
+        "cast_gbps": cast_gbps,
+        "kernel_ms": {n: round(v, 4) for n, v in avg.items()},
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+    }
+
+    if not args.no_stress:
+        result["cast_stress"] = stress_cast(torch, dsg, workloads, dev)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(xb, wb, dyb)
+    print(json.dumps(result), flush=True)
+
+
+def stress_cast(torch, dsg, workloads, dev, iters=10):
+    """Standalone amax+cast of 2^30 bf16 elements to E4M3 and E5M2 (3 B/element)."""
+    n = 1 << 30
+    print("[bench] stress cast 2^30", file=sys.stderr, flush=True)
+    bits = workloads.big_cast_input(n)
+    x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    del bits
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    s = torch.ones(1, dtype=torch.float32, device=dev)
+    am = torch.zeros(1, dtype=torch.float32, device=dev)
+    sat = torch.zeros(1, dtype=torch.int64, device=dev)
+    out = {}
+    stream = torch.cuda.current_stream()
+    for fmt, name in ((dsg.E4M3, "e4m3"), (dsg.E5M2, "e5m2")):
+        dsg.fp8ds_cast(x, fmt, s, q, None, None, am, sat)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            dsg.fp8ds_cast(x, fmt, s, q, None, None, am, sat)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        gbps = 3.0 * n / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                     "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "saturated": int(sat.item())}
+    # standalone amax (2 B/element)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        dsg.fp8ds_amax(x, am)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    out["amax"] = {"ms": round(ms, 4), "GB/s": round(2.0 * n / (ms * 1e-3) / 1e9, 1)}
+    del x, q
+    torch.cuda.empty_cache()
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,246 @@
+// C ABI of the FP8 delayed-scaling Linear: host-side validation, error
+// reporting and dispatch to the HIP launchers.  See include/fp8ds.h for the
+// contract of each entry point.
+
+#include "fp8ds.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FP8DS_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FP8DS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+// Compute units of the current device, cached per device id.
+int num_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bool valid_fmt(int f) { return f == FP8DS_E4M3 || f == FP8DS_E5M2; }
+bool valid_dtype(int t) { return t == FP8DS_F32 || t == FP8DS_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8ds_abi_version(void) { return FP8DS_ABI_VERSION; }
+
+const char* fp8ds_status_string(int status) {
+  switch (status) {
+    case FP8DS_OK: return "ok";
+    case FP8DS_ERR_NULL: return "required pointer is null";
+    case FP8DS_ERR_SHAPE: return "invalid size or leading dimension";
+    case FP8DS_ERR_ENUM: return "enum value out of range";
+    case FP8DS_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case FP8DS_ERR_HIP: return "HIP runtime error";
+    case FP8DS_ERR_UNSUPPORTED: return "unsupported combination";
+    default: return "unknown status";
+  }
+}
+
+const char* fp8ds_last_error(void) { return g_err; }
+
+int fp8ds_amax(const void* x, fp8ds_dtype xt, int64_t n, float* amax, hipStream_t stream) {
+  if (!amax) return fail(FP8DS_ERR_NULL, "fp8ds_amax: amax is null");
+  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "fp8ds_amax: bad dtype %d", (int)xt);
+  if (n < 0 || n > kMaxElems) return fail(FP8DS_ERR_SHAPE, "fp8ds_amax: bad n %lld", (long long)n);
+  if (n > 0 && !x) return fail(FP8DS_ERR_NULL, "fp8ds_amax: x is null");
+  if (n > 0 && !aligned16(x)) return fail(FP8DS_ERR_ALIGN, "fp8ds_amax: x not 16-byte aligned");
+  hipError_t e = fp8ds::launch_prologue(1, nullptr, nullptr, amax, nullptr, stream);
+  if (e == hipSuccess && n > 0)
+    e = fp8ds::launch_cast(x, xt == FP8DS_BF16, 1, n, n, 0, nullptr, nullptr, 0, amax, nullptr,
+                           num_cus(), stream);
+  return hip_status(e, "fp8ds_amax");
+}
+
+int fp8ds_cast(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+               const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
+               uint64_t* sat_count, hipStream_t stream) {
+  if (!scale) return fail(FP8DS_ERR_NULL, "fp8ds_cast: scale is null");
+  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "fp8ds_cast: bad dtype %d", (int)xt);
+  if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "fp8ds_cast: bad format %d", (int)fmt);
+  if (rows < 0 || cols < 0 || (cols > 0 && rows > kMaxElems / cols))
+    return fail(FP8DS_ERR_SHAPE, "fp8ds_cast: bad shape %lld x %lld", (long long)rows,
+                (long long)cols);
+  const int64_t n = rows * cols;
+  if (n > 0) {
+    if (!x || !q) return fail(FP8DS_ERR_NULL, "fp8ds_cast: x or q is null");
+    if (!aligned16(x) || !aligned16(q) || (q_t && !aligned16(q_t)))
+      return fail(FP8DS_ERR_ALIGN, "fp8ds_cast: x, q and q_t must be 16-byte aligned");
+  }
+  hipError_t e = fp8ds::launch_prologue(1, scale, scale_used, amax, sat_count, stream);
+  if (e == hipSuccess && n > 0) {
+    if (q_t)
+      e = fp8ds::launch_cast_transpose(x, xt == FP8DS_BF16, rows, cols, (int)fmt, scale, q, q_t,
+                                       amax, sat_count, stream);
+    else
+      e = fp8ds::launch_cast(x, xt == FP8DS_BF16, 1, n, n, (int)fmt, scale, q, n, amax, sat_count,
+                             num_cus(), stream);
+  }
+  return hip_status(e, "fp8ds_cast");
+}
+
+int fp8ds_cast_batched(const void* x, fp8ds_dtype xt, int64_t batch, int64_t n, int64_t stride_x,
+                       fp8ds_format fmt, const float* scale, uint8_t* q, int64_t stride_q,
+                       float* scale_used, float* amax, uint64_t* sat_count, hipStream_t stream) {
+  if (!scale) return fail(FP8DS_ERR_NULL, "fp8ds_cast_batched: scale is null");
+  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "fp8ds_cast_batched: bad dtype %d", (int)xt);
+  if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "fp8ds_cast_batched: bad format %d", (int)fmt);
+  if (batch < 0 || batch > 65535 || n < 0 || n > kMaxElems)
+    return fail(FP8DS_ERR_SHAPE, "fp8ds_cast_batched: bad batch %lld or n %lld", (long long)batch,
+                (long long)n);
+  if (batch == 0) return ok();
+  const int esz = xt == FP8DS_BF16 ? 2 : 4;
+  if (n > 0) {
+    if (!x || !q) return fail(FP8DS_ERR_NULL, "fp8ds_cast_batched: x or q is null");
+    if (stride_x < n || stride_q < n || stride_x > kMaxElems || stride_q > kMaxElems)
+      return fail(FP8DS_ERR_SHAPE, "fp8ds_cast_batched: strides must be >= n");
+    if (!aligned16(x) || !aligned16(q) || (stride_x * esz) % 16 || stride_q % 16)
+      return fail(FP8DS_ERR_ALIGN, "fp8ds_cast_batched: operands and strides must keep 16-byte "
+                                   "alignment");
+  }
+  hipError_t e = fp8ds::launch_prologue(batch, scale, scale_used, amax, sat_count, stream);
+  if (e == hipSuccess && n > 0)
+    e = fp8ds::launch_cast(x, xt == FP8DS_BF16, batch, n, stride_x, (int)fmt, scale, q, stride_q,
+                           amax, sat_count, num_cus(), stream);
+  return hip_status(e, "fp8ds_cast_batched");
+}
+
+int fp8ds_scale_update(int n_tensors, int hist_len, float* history, int32_t* cursor,
+                       const float* amax, const fp8ds_format* fmt, fp8ds_algo algo, int margin,
+                       float* scale, float* scale_inv, hipStream_t stream) {
+  if (n_tensors < 1 || n_tensors > 4096)
+    return fail(FP8DS_ERR_SHAPE, "fp8ds_scale_update: n_tensors %d not in [1, 4096]", n_tensors);
+  if (hist_len < 1 || hist_len > 65536)
+    return fail(FP8DS_ERR_SHAPE, "fp8ds_scale_update: hist_len %d not in [1, 65536]", hist_len);
+  if (!history || !cursor || !amax || !fmt || !scale)
+    return fail(FP8DS_ERR_NULL, "fp8ds_scale_update: history, cursor, amax, fmt and scale are "
+                                "required");
+  if (algo != FP8DS_ALGO_MAX && algo != FP8DS_ALGO_MOST_RECENT)
+    return fail(FP8DS_ERR_ENUM, "fp8ds_scale_update: bad algo %d", (int)algo);
+  if (margin < -126 || margin > 126)
+    return fail(FP8DS_ERR_SHAPE, "fp8ds_scale_update: margin %d not in [-126, 126]", margin);
+  fp8ds::FmtBits bits;
+  std::memset(&bits, 0, sizeof(bits));
+  for (int t = 0; t < n_tensors; ++t) {
+    if (!valid_fmt(fmt[t]))
+      return fail(FP8DS_ERR_ENUM, "fp8ds_scale_update: bad format %d for tensor %d", (int)fmt[t], t);
+    if (fmt[t] == FP8DS_E5M2) bits.w[t >> 5] |= 1u << (t & 31);
+  }
+  return hip_status(fp8ds::launch_scale_update(n_tensors, hist_len, history, cursor, amax, bits,
+                                               (int)algo, margin, scale, scale_inv, stream),
+                    "fp8ds_scale_update");
+}
+
+static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N,
+                       int64_t K, int64_t batch, const uint8_t* A, fp8ds_format fa, int64_t lda,
+                       int64_t stride_a, const float* scale_a, const uint8_t* B, fp8ds_format fb,
+                       int64_t ldb, int64_t stride_b, const float* scale_b, void* C,
+                       fp8ds_dtype ct, int64_t ldc, int64_t stride_c, float* amax_c,
+                       hipStream_t stream) {
+  if ((opa != FP8DS_OP_N && opa != FP8DS_OP_T) || (opb != FP8DS_OP_N && opb != FP8DS_OP_T))
+    return fail(FP8DS_ERR_ENUM, "%s: bad op", who);
+  if (opa == FP8DS_OP_T && opb == FP8DS_OP_T)
+    return fail(FP8DS_ERR_UNSUPPORTED, "%s: (T, T) is not supported", who);
+  if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8DS_ERR_ENUM, "%s: bad format", who);
+  if (!valid_dtype(ct)) return fail(FP8DS_ERR_ENUM, "%s: bad output dtype", who);
+  const int64_t lim = int64_t(1) << 31;
+  if (M < 0 || N < 0 || K < 0 || M >= lim || N >= lim || K >= lim)
+    return fail(FP8DS_ERR_SHAPE, "%s: bad M/N/K %lld/%lld/%lld", who, (long long)M, (long long)N,
+                (long long)K);
+  if (batch < 0 || batch > 65535) return fail(FP8DS_ERR_SHAPE, "%s: bad batch", who);
+  if (M == 0 || N == 0 || batch == 0) {
+    if (amax_c && batch > 0)
+      return hip_status(fp8ds::launch_prologue(batch, nullptr, nullptr, amax_c, nullptr, stream),
+                        who);
+    return ok();
+  }
+  // Stored shapes: A is [M x K] (N) or [K x M] (T); B is [K x N] (N) or [N x K] (T).
+  const int64_t a_cols = opa == FP8DS_OP_N ? K : M;
+  const int64_t b_cols = opb == FP8DS_OP_N ? N : K;
+  if (lda < a_cols || ldb < b_cols || ldc < N || lda < 1 || ldb < 1)
+    return fail(FP8DS_ERR_SHAPE, "%s: leading dimension too small (lda %lld >= %lld, ldb %lld >= "
+                "%lld, ldc %lld >= %lld)", who, (long long)lda, (long long)a_cols, (long long)ldb,
+                (long long)b_cols, (long long)ldc, (long long)N);
+  if (!C || !scale_a || !scale_b || (K > 0 && (!A || !B)))
+    return fail(FP8DS_ERR_NULL, "%s: A, B, C, scale_a and scale_b are required", who);
+  const int esz = ct == FP8DS_BF16 ? 2 : 4;
+  if ((K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16)) || !aligned16(C) ||
+      (ldc * esz) % 16)
+    return fail(FP8DS_ERR_ALIGN, "%s: A, B, C and lda, ldb, ldc*elem_size must be 16-byte aligned",
+                who);
+  if (batch > 1 && (stride_a % 16 || stride_b % 16 || (stride_c * esz) % 16 || stride_a < 0 ||
+                    stride_b < 0 || stride_c < 0))
+    return fail(FP8DS_ERR_ALIGN, "%s: batch strides must keep 16-byte alignment", who);
+  hipError_t e = hipSuccess;
+  if (amax_c) e = fp8ds::launch_prologue(batch, nullptr, nullptr, amax_c, nullptr, stream);
+  if (e == hipSuccess) {
+    fp8ds::GemmProblem p;
+    p.opa = (int)opa; p.opb = (int)opb;
+    p.M = M; p.N = N; p.K = K;
+    p.A = A; p.fa = (int)fa; p.lda = lda; p.scale_a = scale_a;
+    p.B = B; p.fb = (int)fb; p.ldb = ldb; p.scale_b = scale_b;
+    p.C = C; p.out_bf16 = ct == FP8DS_BF16; p.ldc = ldc; p.amax_c = amax_c;
+    p.batch = batch; p.stride_a = stride_a; p.stride_b = stride_b; p.stride_c = stride_c;
+    e = fp8ds::launch_gemm(p, num_cus(), stream);
+  }
+  return hip_status(e, who);
+}
+
+int fp8ds_gemm(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+               fp8ds_format fa, int64_t lda, const float* scale_a, const uint8_t* B,
+               fp8ds_format fb, int64_t ldb, const float* scale_b, void* C, fp8ds_dtype ct,
+               int64_t ldc, float* amax_c, hipStream_t stream) {
+  return gemm_common("fp8ds_gemm", opa, opb, M, N, K, 1, A, fa, lda, 0, scale_a, B, fb, ldb, 0,
+                     scale_b, C, ct, ldc, 0, amax_c, stream);
+}
+
+int fp8ds_gemm_batched(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K, int64_t batch,
+                       const uint8_t* A, fp8ds_format fa, int64_t lda, int64_t stride_a,
+                       const float* scale_a, const uint8_t* B, fp8ds_format fb, int64_t ldb,
+                       int64_t stride_b, const float* scale_b, void* C, fp8ds_dtype ct,
+                       int64_t ldc, int64_t stride_c, float* amax_c, hipStream_t stream) {
+  return gemm_common("fp8ds_gemm_batched", opa, opb, M, N, K, batch, A, fa, lda, stride_a, scale_a,
+                     B, fb, ldb, stride_b, scale_b, C, ct, ldc, stride_c, amax_c, stream);
+}
+
+}  // extern "C"

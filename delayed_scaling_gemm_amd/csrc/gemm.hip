@@ -1,0 +1,421 @@
+// FP8 x FP8 -> FP32-accumulate GEMM with the dequant epilogue, for gfx950 MFMA.
+//
+// What is computed ("FP8 混合精度训练工程实践" §五: the fp8 linear op multiplies the two
+// quantised operands and divides by the product of their scales; the per-tensor
+// FP8 GEMM row: FP8 in, FP32 accumulate, BF16 out; §三: the three products of a
+// step, Y = X W (NN), dX = dY W^T (NT), dW = X^T dY (TN)):
+//
+//   acc[m][n] = sum_k a(m,k) b(k,n)                 (FP32 accumulation)
+//   C[m][n]   = out( acc[m][n] * fl32(1 / fl32(s_a s_b)) ),  amax_C = max |C|
+//
+// Design (MI355X / CDNA4):
+//  * V_MFMA_F32_16X16X128_F8F6F4: one instruction covers a full 128-deep K tile;
+//    the operand formats (E4M3 / E5M2) are immediates, so HYBRID mixes formats
+//    per operand at full rate.
+//  * Block tile BM x BN x 128, four waves in a 2 x 2 grid, each wave owning a
+//    (BM/2) x (BN/2) sub-tile held entirely in accumulator registers.
+//  * Both operands are staged in LDS as K-contiguous rows of 128 bytes, with the
+//    16-byte chunks of row r XOR-swizzled by ((r ^ (r >> 4)) & 7) so that the
+//    fragment reads (16 consecutive rows, same chunk) and the stores of both
+//    loaders hit distinct banks.
+//  * K-contiguous sources (A in NN/NT, B in NT) are copied 16 bytes per lane;
+//    MN-contiguous sources (B in NN, A and B in TN) are read 16 bytes along M/N
+//    for 8 consecutive k and transposed in registers (byte permutes) on the way
+//    into LDS, so no layout needs an extra HBM pass.
+//  * LDS is double-buffered: the global loads of tile k+1 are in flight while
+//    the MFMAs of tile k run; one barrier per K tile.
+//  * The MFMA is issued with the B fragment as its first operand, so each lane
+//    ends with 4 consecutive output columns of one row: 8-byte BF16 stores.
+//  * Workgroups are remapped so that each XCD (workgroup id mod 8) gets a
+//    contiguous range of tiles, walked in groups of 8 tile-rows, to keep shared
+//    operand panels in that XCD's L2.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8ds {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BK = 128;
+
+struct GemmArgs {
+  int64_t M, N, K;
+  const uint8_t* A;
+  int64_t lda;
+  const float* scale_a;
+  const uint8_t* B;
+  int64_t ldb;
+  const float* scale_b;
+  void* C;
+  int64_t ldc;
+  uint32_t* amax_c;
+  int64_t stride_a, stride_b, stride_c;
+  int tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 4)) & 7; }
+
+// Byte offset in an LDS operand tile of (row r, 16-byte chunk c).
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
+
+// 4x4 byte transpose: out[b] holds byte b of in0..in3 (in0 in the low byte).
+__device__ __forceinline__ void transpose4x4(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t i3,
+                                             uint32_t& o0, uint32_t& o1, uint32_t& o2,
+                                             uint32_t& o3) {
+  // __builtin_amdgcn_perm(hi, lo, sel): byte i of the result is byte sel.byte_i of
+  // the 8-byte value hi:lo (selector 0..3 = lo bytes, 4..7 = hi bytes).
+  uint32_t t0 = __builtin_amdgcn_perm(i1, i0, 0x05010400u);  // i0.b0 i1.b0 i0.b1 i1.b1
+  uint32_t t1 = __builtin_amdgcn_perm(i1, i0, 0x07030602u);  // i0.b2 i1.b2 i0.b3 i1.b3
+  uint32_t t2 = __builtin_amdgcn_perm(i3, i2, 0x05010400u);  // i2.b0 i3.b0 i2.b1 i3.b1
+  uint32_t t3 = __builtin_amdgcn_perm(i3, i2, 0x07030602u);  // i2.b2 i3.b2 i2.b3 i3.b3
+  o0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);           // i0.b0 i1.b0 i2.b0 i3.b0
+  o1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);           // i0.b1 i1.b1 i2.b1 i3.b1
+  o2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);           // i0.b2 ...
+  o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);           // i0.b3 ...
+}
+
+// ------------------------------------------------------------------ loaders
+
+// K-contiguous operand: rows [row0, row0 + ROWS) of a [rows x K] byte matrix
+// (leading dimension ld), k in [k0, k0 + 128).  Each lane moves 16-byte chunks.
+template <int ROWS, int NT>
+struct LoaderKC {
+  static constexpr int kChunks = ROWS * 8 / NT;
+  u32x4 v[kChunks];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ src, int64_t ld, int64_t row0,
+                                       int64_t rows, int64_t k0, int64_t K, int tid) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int q = tid + NT * i;
+      const int r = q >> 3, c = q & 7;
+      const int64_t gr = row0 + r;
+      const int64_t gk = k0 + c * 16;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (gr < rows && gk < K) {
+        val = *reinterpret_cast<const u32x4*>(src + gr * ld + gk);
+        const int64_t valid = K - gk;
+        if (valid < 16) {  // ragged K: zero the bytes past K
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int64_t vb = valid - 4 * w;
+            const uint32_t keep = vb >= 4 ? 0xFFFFFFFFu : (vb <= 0 ? 0u : ((1u << (8 * vb)) - 1u));
+            val[w] &= keep;
+          }
+        }
+      }
+      v[i] = val;
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int q = tid + NT * i;
+      const int r = q >> 3, c = q & 7;
+      *reinterpret_cast<u32x4*>(lds + lds_off(r, c)) = v[i];
+    }
+  }
+};
+
+// MN-contiguous operand: element (k, r) at src[(k0 + k) * ld + row0 + r]; the tile
+// needs rows r in [0, ROWS) of 128 K-bytes.  A unit is 8 k x 16 r bytes: 8 loads of
+// 16 bytes along r, transposed into 16 rows of 8 K-bytes.
+template <int ROWS, int NT>
+struct LoaderMN {
+  // ROWS units of 8k x 16r bytes per tile; with ROWS < NT some threads idle.
+  static constexpr int kUnits = (ROWS + NT - 1) / NT;
+  static_assert(ROWS % NT == 0 || NT % ROWS == 0, "tile rows and thread count must nest");
+  u32x4 v[kUnits][8];
+
+  // unit u -> 16-row chunk mc and 8-deep k group kg, lanes ordered so that 8
+  // consecutive lanes read 128 contiguous bytes of one k row.
+  __device__ __forceinline__ static void unit_coords(int u, int& mc, int& kg) {
+    mc = (u & 7) + ((u >> 7) << 3);
+    kg = (u >> 3) & 15;
+  }
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ src, int64_t ld, int64_t row0,
+                                       int64_t rows, int64_t k0, int64_t K, int tid) {
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      if (tid + NT * i >= ROWS) break;
+      int mc, kg;
+      unit_coords(tid + NT * i, mc, kg);
+      const int64_t gr = row0 + mc * 16;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int64_t gk = k0 + kg * 8 + kk;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (gk < K && gr < rows) {
+          const int64_t valid = rows - gr;
+          if (valid >= 16) {
+            val = *reinterpret_cast<const u32x4*>(src + gk * ld + gr);
+          } else {  // ragged M/N edge: byte loads of the valid part
+            const uint8_t* p = src + gk * ld + gr;
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+              const uint32_t byte = b < valid ? (uint32_t)p[b] : 0u;
+              val[b >> 2] |= byte << (8 * (b & 3));
+            }
+          }
+        }
+        v[i][kk] = val;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      if (tid + NT * i >= ROWS) break;
+      int mc, kg;
+      unit_coords(tid + NT * i, mc, kg);
+      const int c = kg >> 1;         // 16-byte chunk of the K row
+      const int half = (kg & 1) * 8; // 8-byte half within it
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // dword column j: rows 4j .. 4j+3 of the unit
+        uint32_t lo[4], hi[4];
+        transpose4x4(v[i][0][j], v[i][1][j], v[i][2][j], v[i][3][j], lo[0], lo[1], lo[2], lo[3]);
+        transpose4x4(v[i][4][j], v[i][5][j], v[i][6][j], v[i][7][j], hi[0], hi[1], hi[2], hi[3]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = mc * 16 + 4 * j + b;
+          u32x2 w = {lo[b], hi[b]};
+          *reinterpret_cast<u32x2*>(lds + lds_off(r, c) + half) = w;
+        }
+      }
+    }
+  }
+};
+
+template <bool KC, int ROWS, int NT>
+struct LoaderSel;
+template <int ROWS, int NT>
+struct LoaderSel<true, ROWS, NT> { using type = LoaderKC<ROWS, NT>; };
+template <int ROWS, int NT>
+struct LoaderSel<false, ROWS, NT> { using type = LoaderMN<ROWS, NT>; };
+
+// ------------------------------------------------------------------ tile order
+
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  int logical = wg;
+  if (T >= 8) {
+    // XCD x = wg % 8 takes the contiguous logical range [start_x, start_x + cnt_x).
+    const int q = T >> 3, rem = T & 7;
+    const int x = wg & 7, idx = wg >> 3;
+    logical = x * q + min(x, rem) + idx;
+  }
+  constexpr int GM = 8;  // tile-rows per group
+  const int per_group = GM * tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int in_group = logical - group * per_group;
+  tm = first_m + in_group % gsz;
+  tn = in_group / gsz;
+}
+
+// ------------------------------------------------------------------ the kernel
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return ((b >> 16) & 0x8000u) | 0x7FC0u;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
+  constexpr int NT = 256;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * BK];
+  __shared__ uint32_t red[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t bz = blockIdx.y;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const uint8_t* A = p.A + bz * p.stride_a;
+  const uint8_t* B = p.B + bz * p.stride_b;
+
+  typename LoaderSel<A_KC, BM, NT>::type la;
+  typename LoaderSel<B_KC, BN, NT>::type lb;
+
+  v4f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = {0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (int)((K + BK - 1) / BK);
+  if (nk > 0) {
+    la.load(A, p.lda, m0, M, 0, K, tid);
+    lb.load(B, p.ldb, n0, N, 0, K, tid);
+    la.store(lds_a[0], tid);
+    lb.store(lds_b[0], tid);
+  }
+  __syncthreads();
+
+  const int fr = lane & 15;         // fragment row within a 16-row block
+  const int fc = (lane >> 4) * 2;   // first 16-byte K chunk of this lane
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      la.load(A, p.lda, m0, M, (int64_t)(kt + 1) * BK, K, tid);
+      lb.load(B, p.ldb, n0, N, (int64_t)(kt + 1) * BK, K, tid);
+    }
+    const uint8_t* sa = lds_a[cur];
+    const uint8_t* sb = lds_b[cur];
+    v8i bf[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WTN + j * 16 + fr;
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(sb + lds_off(r, fc));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(sb + lds_off(r, fc + 1));
+      bf[j] = v8i{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                  (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 16 + fr;
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(sa + lds_off(r, fc));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(sa + lds_off(r, fc + 1));
+      const v8i af = v8i{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        // first operand = B fragment (format FB), second = A fragment (format FA):
+        // the result is the C^T block, i.e. lane holds 4 consecutive columns.
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], FB, FA,
+                                                                      0, 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) {
+      la.store(lds_a[cur ^ 1], tid);
+      lb.store(lds_b[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const float d = __fdiv_rn(1.0f, p.scale_a[bz] * p.scale_b[bz]);
+  uint32_t amax = 0;
+  const int ccol = (lane >> 4) * 4;  // first of this lane's 4 columns in a 16-block
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + wm * WTM + i * 16 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * WTN + j * 16 + ccol;
+      if (n >= N) continue;
+      const float y0 = acc[i][j][0] * d, y1 = acc[i][j][1] * d;
+      const float y2 = acc[i][j][2] * d, y3 = acc[i][j][3] * d;
+      if constexpr (OUT_BF16) {
+        uint16_t* C = static_cast<uint16_t*>(p.C) + bz * p.stride_c + m * p.ldc + n;
+        const uint32_t h0 = f32_to_bf16_rne(y0), h1 = f32_to_bf16_rne(y1);
+        const uint32_t h2 = f32_to_bf16_rne(y2), h3 = f32_to_bf16_rne(y3);
+        if (n + 3 < N) {
+          *reinterpret_cast<u32x2*>(C) = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
+          amax = max(amax, max(max(h0 & 0x7FFFu, h1 & 0x7FFFu), max(h2 & 0x7FFFu, h3 & 0x7FFFu)));
+        } else {
+          const uint32_t hv[4] = {h0, h1, h2, h3};
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n + v < N) {
+              C[v] = (uint16_t)hv[v];
+              amax = max(amax, hv[v] & 0x7FFFu);
+            }
+        }
+      } else {
+        float* C = static_cast<float*>(p.C) + bz * p.stride_c + m * p.ldc + n;
+        const float yv[4] = {y0, y1, y2, y3};
+        if (n + 3 < N) {
+          *reinterpret_cast<v4f*>(C) = v4f{y0, y1, y2, y3};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) amax = max(amax, __float_as_uint(yv[v]) & 0x7FFFFFFFu);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n + v < N) {
+              C[v] = yv[v];
+              amax = max(amax, __float_as_uint(yv[v]) & 0x7FFFFFFFu);
+            }
+        }
+      }
+    }
+  }
+  if (p.amax_c) {
+    if constexpr (OUT_BF16) amax <<= 16;
+    amax = wave_max_u32(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
+      atomicMax(p.amax_c + bz, canonical_amax_bits(m));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool OUT_BF16>
+static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
+  GemmArgs a;
+  a.M = q.M; a.N = q.N; a.K = q.K;
+  a.A = q.A; a.lda = q.lda; a.scale_a = q.scale_a;
+  a.B = q.B; a.ldb = q.ldb; a.scale_b = q.scale_b;
+  a.C = q.C; a.ldc = q.ldc; a.amax_c = reinterpret_cast<uint32_t*>(q.amax_c);
+  a.stride_a = q.stride_a; a.stride_b = q.stride_b; a.stride_c = q.stride_c;
+  a.tiles_m = (int)((q.M + BM - 1) / BM);
+  a.tiles_n = (int)((q.N + BN - 1) / BN);
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)q.batch);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, OUT_BF16>), grid, dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, bool A_KC, bool B_KC>
+static hipError_t launch_layout(const GemmProblem& q, hipStream_t s) {
+#define FP8DS_GEMM_CASE(FA_, FB_)                                                          \
+  if (q.fa == FA_ && q.fb == FB_)                                                          \
+    return q.out_bf16 ? launch_cfg<BM, BN, A_KC, B_KC, FA_, FB_, true>(q, s)               \
+                      : launch_cfg<BM, BN, A_KC, B_KC, FA_, FB_, false>(q, s);
+  FP8DS_GEMM_CASE(kE4M3, kE4M3)
+  FP8DS_GEMM_CASE(kE4M3, kE5M2)
+  FP8DS_GEMM_CASE(kE5M2, kE4M3)
+  FP8DS_GEMM_CASE(kE5M2, kE5M2)
+#undef FP8DS_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int BM, int BN>
+static hipError_t launch_tile(const GemmProblem& q, hipStream_t s) {
+  if (q.opa == 0 && q.opb == 0) return launch_layout<BM, BN, true, false>(q, s);  // NN
+  if (q.opa == 0 && q.opb == 1) return launch_layout<BM, BN, true, true>(q, s);   // NT
+  if (q.opa == 1 && q.opb == 0) return launch_layout<BM, BN, false, false>(q, s); // TN
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(const GemmProblem& q, int num_cus, hipStream_t stream) {
+  if (q.M <= 0 || q.N <= 0 || q.batch <= 0) return hipSuccess;
+  const int64_t big_tiles = ((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
+  if (big_tiles >= num_cus) return launch_tile<256, 256>(q, stream);
+  return launch_tile<128, 128>(q, stream);
+}
+
+}  // namespace fp8ds

@@ -1,0 +1,56 @@
+// Host-side launchers of the HIP kernels (internal to the library; the public
+// interface is the C ABI in include/fp8ds.h).  All launchers enqueue work on
+// `stream` and return the launch status; arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8ds {
+
+// scale_used[i] = scale[i]; amax[i] = 0; sat[i] = 0 for i < count (null outputs skipped).
+hipError_t launch_prologue(int64_t count, const float* scale, float* scale_used, float* amax,
+                           uint64_t* sat, hipStream_t stream);
+
+// Fused amax + cast over `batch` tensors of n elements (q == nullptr: amax only).
+// amax and sat must have been reset by launch_prologue.
+hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride_x,
+                       int fmt, const float* scale, uint8_t* q, int64_t stride_q, float* amax,
+                       uint64_t* sat, int num_cus, hipStream_t stream);
+
+// Cast of a [rows x cols] tensor writing q and its transpose qt.
+hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
+                                 const float* scale, uint8_t* q, uint8_t* qt, float* amax,
+                                 uint64_t* sat, hipStream_t stream);
+
+// History push + window reduction + next scale for n tensors.
+// fmt_bits: bit t set = tensor t is E5M2.
+struct FmtBits {
+  uint32_t w[128];
+};
+hipError_t launch_scale_update(int n, int hist_len, float* history, int32_t* cursor,
+                               const float* amax, const FmtBits& fmt, int algo, int margin,
+                               float* scale, float* scale_inv, hipStream_t stream);
+
+// FP8 GEMM.  opa/opb: 0 = N, 1 = T.  out_bf16: BF16 output, else FP32.
+struct GemmProblem {
+  int opa, opb;
+  int64_t M, N, K;
+  const uint8_t* A;
+  int fa;
+  int64_t lda;
+  const float* scale_a;
+  const uint8_t* B;
+  int fb;
+  int64_t ldb;
+  const float* scale_b;
+  void* C;
+  bool out_bf16;
+  int64_t ldc;
+  float* amax_c;  // reset by the caller
+  int64_t batch;
+  int64_t stride_a, stride_b, stride_c;  // bytes, bytes, elements
+};
+hipError_t launch_gemm(const GemmProblem& p, int num_cus, hipStream_t stream);
+
+}  // namespace fp8ds

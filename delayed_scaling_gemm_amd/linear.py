@@ -1,0 +1,99 @@
+"""One FP8 delayed-scaling Linear step composed from the C-ABI calls.
+
+Host-side orchestration only (every arithmetic step runs in the HIP library):
+
+  fwd:  cast X (E4M3), cast W (E4M3)          -> Xq, Wq, amax_X, amax_W, scale snapshots
+        Y  = Xq . Wq         (NN)             -> BF16 Y + amax_Y
+  bwd:  cast dY (E5M2)                        -> dYq, amax_dY
+        dX = dYq . Wq^T      (NT)             -> BF16 dX
+        dW = Xq^T . dYq      (TN)             -> BF16 dW
+  end:  one scale update over the X, W, dY histories -> scales of the next step
+
+This is the HYBRID recipe ("LLM FP8 微调上线生产实战" §核心原理: E4M3 for forward
+tensors, E5M2 for gradients) with delayed scaling: each cast uses the scale that
+the previous steps' amax history produced, and the GEMMs use the snapshot of the
+scale their operands were cast with ("FP8 混合精度训练工程实践" §四 动态缩放).
+W is stored [in, out], so the forward product is NN.  The backward products
+reuse the forward FP8 bytes of X and W.
+
+Everything stays on the device and on one stream: there is no host
+synchronisation inside a step.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import (ALGO_MAX, E4M3, E5M2, OP_N, OP_T, fp8ds_cast, fp8ds_gemm, fp8ds_scale_update)
+
+X, W, DY = 0, 1, 2
+
+
+class DelayedScalingLinear:
+    """Delayed-scaling state of one Linear (history ring, cursor and scale per
+    tensor X, W, dY) and its fwd(+bwd) step."""
+
+    def __init__(self, hist_len: int = 16, algo: int = ALGO_MAX, margin: int = 0,
+                 fmts=(E4M3, E4M3, E5M2), device="cuda"):
+        self.hist_len = hist_len
+        self.algo = algo
+        self.margin = margin
+        self.fmts = tuple(fmts)
+        self.device = torch.device(device)
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.history = torch.zeros(3, hist_len, **f32)
+        self.cursor = torch.zeros(3, dtype=torch.int32, device=self.device)
+        self.scale = torch.ones(3, **f32)
+        self.scale_used = torch.zeros(3, **f32)
+        self.amax = torch.zeros(3, **f32)
+        self.sat = torch.zeros(3, dtype=torch.int64, device=self.device)
+        self.amax_y = torch.zeros(1, **f32)
+        self._bufs = {}
+
+    def _buf(self, name, shape, dtype):
+        t = self._bufs.get(name)
+        if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+            t = torch.empty(shape, dtype=dtype, device=self.device)
+            self._bufs[name] = t
+        return t
+
+    def state(self):
+        """Copies of the scaling state (history, cursor, scale)."""
+        return self.history.clone(), self.cursor.clone(), self.scale.clone()
+
+    def step(self, x, w, dy=None, stream=None):
+        """One step; returns a dict with the FP8 operands and the BF16 outputs."""
+        M, K = x.shape
+        K2, N = w.shape
+        assert K == K2, "x is [M, in] and w is [in, out]"
+        u8 = torch.uint8
+        xq = self._buf("xq", (M, K), u8)
+        wq = self._buf("wq", (K, N), u8)
+        y = self._buf("y", (M, N), torch.bfloat16)
+        s, su, am, sat = self.scale, self.scale_used, self.amax, self.sat
+        fp8ds_cast(x, self.fmts[X], s[X:X + 1], xq, None, su[X:X + 1], am[X:X + 1], sat[X:X + 1],
+                   stream)
+        fp8ds_cast(w, self.fmts[W], s[W:W + 1], wq, None, su[W:W + 1], am[W:W + 1], sat[W:W + 1],
+                   stream)
+        fp8ds_gemm(OP_N, OP_N, M, N, K, xq, self.fmts[X], K, su[X:X + 1], wq, self.fmts[W], N,
+                   su[W:W + 1], y, N, self.amax_y, stream)
+        out = {"xq": xq, "wq": wq, "y": y}
+        n_upd = 2
+        if dy is not None:
+            assert tuple(dy.shape) == (M, N)
+            dyq = self._buf("dyq", (M, N), u8)
+            dx = self._buf("dx", (M, K), torch.bfloat16)
+            dw = self._buf("dw", (K, N), torch.bfloat16)
+            fp8ds_cast(dy, self.fmts[DY], s[DY:DY + 1], dyq, None, su[DY:DY + 1], am[DY:DY + 1],
+                       sat[DY:DY + 1], stream)
+            # dX[M, K] = dYq[M, N] . Wq^T   (Wq stored [K, N] = [N' x K'] -> op T)
+            fp8ds_gemm(OP_N, OP_T, M, K, N, dyq, self.fmts[DY], N, su[DY:DY + 1], wq, self.fmts[W],
+                       N, su[W:W + 1], dx, K, None, stream)
+            # dW[K, N] = Xq^T . dYq         (Xq stored [M, K] = [K' x M'] -> op T)
+            fp8ds_gemm(OP_T, OP_N, K, N, M, xq, self.fmts[X], K, su[X:X + 1], dyq, self.fmts[DY],
+                       N, su[DY:DY + 1], dw, N, None, stream)
+            out.update(dyq=dyq, dx=dx, dw=dw)
+            n_upd = 3
+        fp8ds_scale_update(self.history[:n_upd], self.cursor[:n_upd], am[:n_upd],
+                           self.fmts[:n_upd], self.algo, self.margin, s[:n_upd], None, stream)
+        return out

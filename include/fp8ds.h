@@ -1,0 +1,219 @@
+/*
+ * fp8ds.h -- C ABI of the FP8 delayed-scaling Linear for AMD MI355X (gfx950).
+ *
+ * The library computes the hot path of an FP8 training Linear with delayed
+ * per-tensor scaling:
+ *
+ *   amax of a BF16/FP32 tensor  ->  scale from an amax-history window
+ *   ->  saturating round-to-nearest-even cast to OCP E4M3 / E5M2
+ *   ->  FP8 x FP8 GEMM with FP32 accumulation (NN, NT, TN)
+ *   ->  dequant by 1/(s_a * s_b) into BF16, with the output amax fused.
+ *
+ * Sources (cited by page title and section):
+ *   [P2] "FP8 混合精度训练工程实践：从 H100 到大模型训练的范式跃迁" (ybb.press)
+ *   [P3] "LLM FP8 微调上线生产实战：用 Amax Scaling、层级白名单与 BF16 回退守住收敛"
+ *        (oh-bug.com)
+ *   [OCP] the OCP 8-bit floating point formats (Micikevicius et al., "FP8 Formats
+ *        for Deep Learning", in [P3]'s reference list) for special values.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless a parameter says "host".  The caller
+ *     owns every buffer; the library keeps no pointer after the call returns and
+ *     allocates no device memory.
+ *   - Every call is asynchronous on `stream` (0 = the null stream): it validates
+ *     its arguments on the host, enqueues kernels and returns.  Device-side
+ *     results are ready after the stream is synchronised.
+ *   - Return value: FP8DS_OK (0) or a negative fp8ds_status.  On failure nothing
+ *     has been enqueued (validation) or a launch failed (FP8DS_ERR_HIP), and
+ *     fp8ds_last_error() returns a thread-local message.  No C++ exception,
+ *     abort or exit crosses the ABI.  A device fault (e.g. a pointer that does
+ *     not span the stated size) surfaces at the caller's next synchronisation.
+ *   - Zero-size inputs are legal no-ops that still write their scalar outputs
+ *     (amax = 0, saturation count = 0, scale_used = *scale).
+ *   - Row-major layouts; `ld*` are leading dimensions in elements.
+ *   - Calls that write the same output buffers must not overlap (the fused
+ *     amax / counters are reset by the call that writes them).
+ */
+#ifndef FP8DS_H
+#define FP8DS_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8DS_ABI_VERSION 1
+
+typedef enum {
+  FP8DS_OK = 0,
+  FP8DS_ERR_NULL = -1,        /* a required pointer is NULL */
+  FP8DS_ERR_SHAPE = -2,       /* negative / overflowing size, or ld too small */
+  FP8DS_ERR_ENUM = -3,        /* a format, dtype, op or algo value out of range */
+  FP8DS_ERR_ALIGN = -4,       /* pointer or leading dimension not 16-byte aligned */
+  FP8DS_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+  FP8DS_ERR_UNSUPPORTED = -6  /* valid but unsupported combination (e.g. TT) */
+} fp8ds_status;
+
+/* FP8 formats ([P2] §一 "FP8 格式设计"; [P3] §核心原理 "E4M3 与 E5M2 承担不同职责"):
+ * E4M3: bias 7, largest finite 448, no infinity (OCP "fn" variant, [OCP]).
+ * E5M2: bias 15, largest finite 57344, with +-inf ([OCP]). */
+typedef enum { FP8DS_E4M3 = 0, FP8DS_E5M2 = 1 } fp8ds_format;
+
+/* High-precision element types of inputs and GEMM outputs. */
+typedef enum { FP8DS_F32 = 0, FP8DS_BF16 = 1 } fp8ds_dtype;
+
+/* Window reductions of the amax history ([P3] §核心原理 "Delayed Scaling
+ * 用历史换取稳定性", the table of strategies: max over the window, or the most
+ * recent value). */
+typedef enum { FP8DS_ALGO_MAX = 0, FP8DS_ALGO_MOST_RECENT = 1 } fp8ds_algo;
+
+/* GEMM operand layout: N = used as stored, T = the stored array is transposed. */
+typedef enum { FP8DS_OP_N = 0, FP8DS_OP_T = 1 } fp8ds_op;
+
+/* ABI version (FP8DS_ABI_VERSION of the built library). */
+int fp8ds_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* fp8ds_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* fp8ds_last_error(void);
+
+/*
+ * fp8ds_amax -- amax = max_i |x_i| of the unscaled tensor.
+ * [P2] §四 "动态缩放" (the quantize step takes the maximum absolute value of the
+ * high-precision tensor); [P3] §核心原理 "Scale 决定数值是否进入可表示区间".
+ *
+ *   x      device, n elements of `xt` (BF16 or FP32), 16-byte aligned.
+ *   n      element count, n >= 0.
+ *   amax   device, 1 float: overwritten with the result.  Exact (the maximum is
+ *          one of the inputs).  NaN anywhere gives the canonical qNaN 0x7FC00000;
+ *          otherwise +inf if any element is infinite; 0 for n == 0; |-0| = +0.
+ */
+int fp8ds_amax(const void* x, fp8ds_dtype xt, int64_t n, float* amax, hipStream_t stream);
+
+/*
+ * fp8ds_cast -- scaled saturating cast of a [rows x cols] tensor to FP8, with the
+ * input amax fused into the same pass.
+ * [P2] §四 "动态缩放" (quantize: multiply by the scale, clamp to the format's
+ * range, convert); [P2] §五 (the fp8 linear op casts input and weight with their
+ * scales before the product).
+ *
+ *   q[i] = encode_fmt( fl32(x[i] * (*scale)) )
+ * where fl32 is one IEEE fp32 multiply (round to nearest even) and encode is the
+ * saturating round-to-nearest-even conversion: |v| > max (infinities included)
+ * gives the largest finite code of v's sign, NaN gives 0x7F | sign << 7, and the
+ * sign is kept on underflow to zero.
+ *
+ *   x          device, rows*cols elements of `xt`, row-major, contiguous, 16-byte aligned.
+ *   rows,cols  >= 0.
+ *   fmt        target format.
+ *   scale      device, 1 float: the delayed scale of this step (read once).
+ *   q          device, rows*cols bytes, row-major, 16-byte aligned.
+ *   q_t        device or NULL: if non-NULL also receives the transposed copy,
+ *              [cols x rows] row-major (q_t[c*rows + r] == q[r*cols + c]), for GEMM
+ *              operands the caller wants K-contiguous.  16-byte aligned.
+ *   scale_used device or NULL: receives a copy of *scale -- the snapshot the FP8
+ *              bytes were made with.  GEMMs must be given this snapshot, because
+ *              fp8ds_scale_update overwrites *scale for the next step.
+ *   amax       device or NULL: receives max|x| of the UNSCALED input (as fp8ds_amax).
+ *   sat_count  device or NULL: receives #{i : |fl32(x[i]*scale)| > max}
+ *              (infinities counted, NaN not).
+ */
+int fp8ds_cast(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+               const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
+               uint64_t* sat_count, hipStream_t stream);
+
+/*
+ * fp8ds_cast_batched -- `batch` independent casts of equal size n, each with its
+ * own scale (the per-problem scales of a batch of small Linears).
+ *
+ *   x          device, batch tensors of n elements, tensor b at x + b*stride_x elements
+ *              (stride_x >= n, stride_x*elem_size a multiple of 16).
+ *   scale      device [batch].
+ *   q          device, tensor b at q + b*stride_q bytes (stride_q >= n, multiple of 16).
+ *   scale_used, amax: device [batch] or NULL.   sat_count: device [batch] or NULL.
+ * Semantics per tensor as fp8ds_cast without the transposed copy.
+ */
+int fp8ds_cast_batched(const void* x, fp8ds_dtype xt, int64_t batch, int64_t n, int64_t stride_x,
+                       fp8ds_format fmt, const float* scale, uint8_t* q, int64_t stride_q,
+                       float* scale_used, float* amax, uint64_t* sat_count, hipStream_t stream);
+
+/*
+ * fp8ds_scale_update -- push this step's amax into each tensor's history ring and
+ * compute the scale of the next step.
+ * [P3] §核心原理 "Scale 决定数值是否进入可表示区间" (scale = (FP8_MAX/amax)/2^margin);
+ * [P3] §核心原理 "Delayed Scaling 用历史换取稳定性" (history window, max or
+ * most_recent); [P2] §四 "Delayed Scaling 的工程细节" (ring buffer with a cursor
+ * advanced modulo the history length; scale 1.0 when the history maximum is not
+ * positive).
+ *
+ * For each tensor t in [0, n_tensors):
+ *   history[t*hist_len + cursor[t]] = amax[t];  cursor[t] = (cursor[t] + 1) % hist_len;
+ *   w = max over history[t*hist_len .. +hist_len)  (ALGO_MAX; NaN propagates)
+ *     | amax[t]                                       (ALGO_MOST_RECENT);
+ *   scale[t] = ldexp(fl32(FP8_MAX(fmt[t]) / w), -margin)   if w is finite and > 0 and
+ *              the result is finite and > 0;   1.0 otherwise.
+ * The quotient is one correctly rounded fp32 division.
+ *
+ *   n_tensors  1 .. 4096.          hist_len  1 .. 65536.
+ *   history    device [n_tensors][hist_len] fp32, in/out (initially zeros).
+ *   cursor     device [n_tensors] int32, in/out (initially 0; must be in [0, hist_len)).
+ *   amax       device [n_tensors] fp32 (e.g. the amax outputs of fp8ds_cast).
+ *   fmt        HOST [n_tensors] fp8ds_format, read during the call only.
+ *   algo       window reduction.       margin  integer exponent, -126..126.
+ *   scale      device [n_tensors] fp32, overwritten with the next step's scale.
+ *   scale_inv  device [n_tensors] or NULL: receives fl32(1 / scale).
+ */
+int fp8ds_scale_update(int n_tensors, int hist_len, float* history, int32_t* cursor,
+                       const float* amax, const fp8ds_format* fmt, fp8ds_algo algo, int margin,
+                       float* scale, float* scale_inv, hipStream_t stream);
+
+/*
+ * fp8ds_gemm -- C = dequant( op(A) . op(B) ), FP8 x FP8 with FP32 accumulation.
+ * [P2] §五 (the fp8 linear op: FP8 product divided by the product of the two
+ * scales; the per-tensor FP8 GEMM: FP8 inputs, FP32 accumulate, BF16 output);
+ * [P2] §三 (the three products of a training step: Y = X W, dX = dY W^T,
+ * dW = X^T dY; HYBRID formats per [P3] §核心原理: E4M3 forward, E5M2 gradients).
+ *
+ *   acc[i][j] = sum_k a(i,k) * b(k,j)   over decoded FP8 values, FP32 accumulation
+ *   C[i][j]   = convert_ct( acc[i][j] * d ),  d = fl32(1 / fl32((*scale_a) * (*scale_b)))
+ * with round-to-nearest-even to BF16 (ct = BF16) or no rounding (ct = F32).
+ *
+ *   opa, opb   (N,N), (N,T) or (T,N); (T,T) returns FP8DS_ERR_UNSUPPORTED.
+ *   M, N, K    >= 0.  op(A) is M x K, op(B) is K x N, C is M x N.
+ *   A          device: opa == N: [M x K] with lda >= K;  opa == T: [K x M] with lda >= M.
+ *   B          device: opb == N: [K x N] with ldb >= N;  opb == T: [N x K] with ldb >= K.
+ *   fa, fb     formats of A and B, independently E4M3 or E5M2.
+ *   lda, ldb   multiples of 16 bytes; A and B 16-byte aligned.
+ *   scale_a/b  device, 1 float each: the scale snapshots the operands were cast with.
+ *   C          device [M x N] of `ct` with ldc >= N; C and ldc*elem_size 16-byte aligned.
+ *   amax_c     device or NULL: receives max |C[i][j]| of the stored output (NaN as
+ *              fp8ds_amax).
+ */
+int fp8ds_gemm(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K,
+               const uint8_t* A, fp8ds_format fa, int64_t lda, const float* scale_a,
+               const uint8_t* B, fp8ds_format fb, int64_t ldb, const float* scale_b,
+               void* C, fp8ds_dtype ct, int64_t ldc, float* amax_c, hipStream_t stream);
+
+/*
+ * fp8ds_gemm_batched -- `batch` independent GEMMs of one shape, each with its own
+ * scales and output amax (many small Linears in one launch).
+ * Problem b uses A + b*stride_a, B + b*stride_b (bytes), C + b*stride_c (elements),
+ * scale_a[b], scale_b[b], amax_c[b]; otherwise as fp8ds_gemm.  Strides must keep
+ * every operand 16-byte aligned.
+ */
+int fp8ds_gemm_batched(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K, int64_t batch,
+                       const uint8_t* A, fp8ds_format fa, int64_t lda, int64_t stride_a,
+                       const float* scale_a, const uint8_t* B, fp8ds_format fb, int64_t ldb,
+                       int64_t stride_b, const float* scale_b, void* C, fp8ds_dtype ct,
+                       int64_t ldc, int64_t stride_c, float* amax_c, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8DS_H */

@@ -142,7 +142,14 @@ def cast(x: np.ndarray, scale, fmt: int):
     number of elements with ``|fl32(x * s)| > max`` (infinities counted, NaN not).
     """
     y = scaled_product_f32(x, np.float32(scale))
-    codes = encode(y, fmt)
+    return encode(y, fmt), _count_above_max(y, fmt)
+
+
+def _count_above_max(y: np.ndarray, fmt: int) -> int:
     with np.errstate(invalid="ignore"):
-        sat = int(np.count_nonzero(np.abs(y.astype(np.float64)) > fmt_max(fmt)))
-    return codes, sat
+        return int(np.count_nonzero(np.abs(y.astype(np.float64)) > fmt_max(fmt)))
+
+
+def saturation_count(x: np.ndarray, scale, fmt: int) -> int:
+    """The saturation count of :func:`cast` alone (no encoding): ``#{|fl32(x*s)| > max}``."""
+    return _count_above_max(scaled_product_f32(x, np.float32(scale)), fmt)

@@ -1,0 +1,87 @@
+"""The C-ABI library loads and exports every symbol include/fp8ds.h declares, and its
+host-side validation rejects bad arguments before touching the GPU (CPU only:
+no compute call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import delayed_scaling_gemm_amd as dsg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8ds.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsg.LIB_PATH),
+                                reason="libfp8ds.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8ds_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fp8ds_amax", "fp8ds_cast", "fp8ds_cast_batched", "fp8ds_scale_update",
+              "fp8ds_gemm", "fp8ds_gemm_batched", "fp8ds_status_string", "fp8ds_last_error",
+              "fp8ds_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dsg.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert dsg.abi_version() == 1
+
+
+def test_status_strings():
+    L = dsg.lib()
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert L.fp8ds_status_string(s)
+    assert L.fp8ds_status_string(-99) == b"unknown status"
+
+
+def _status(call):
+    return call, dsg.lib().fp8ds_last_error().decode()
+
+
+def test_validation_errors_without_gpu():
+    L = dsg.lib()
+    p = 0x1000  # aligned, never dereferenced: validation fails first
+    st, msg = _status(L.fp8ds_amax(p, 1, 16, None, None))
+    assert st == -1 and "amax" in msg
+    assert L.fp8ds_amax(p, 7, 16, p, None) == -3
+    assert L.fp8ds_amax(p, 1, -1, p, None) == -2
+    assert L.fp8ds_amax(p + 2, 1, 16, p, None) == -4
+    # cast
+    assert L.fp8ds_cast(p, 1, 4, 4, 0, None, p, None, None, None, None, None) == -1
+    assert L.fp8ds_cast(p, 1, 4, 4, 5, p, p, None, None, None, None, None) == -3
+    assert L.fp8ds_cast(p, 1, -4, 4, 0, p, p, None, None, None, None, None) == -2
+    assert L.fp8ds_cast(p, 1, 4, 4, 0, p, p + 8, None, None, None, None, None) == -4
+    assert L.fp8ds_cast(None, 1, 4, 4, 0, p, p, None, None, None, None, None) == -1
+    # scale update
+    fm = (ctypes.c_int * 2)(0, 1)
+    fmp = ctypes.cast(fm, ctypes.c_void_p)
+    assert L.fp8ds_scale_update(0, 16, p, p, p, fmp, 0, 0, p, None, None) == -2
+    assert L.fp8ds_scale_update(2, 0, p, p, p, fmp, 0, 0, p, None, None) == -2
+    assert L.fp8ds_scale_update(2, 16, p, p, p, fmp, 3, 0, p, None, None) == -3
+    assert L.fp8ds_scale_update(2, 16, p, p, p, fmp, 0, 200, p, None, None) == -2
+    assert L.fp8ds_scale_update(2, 16, None, p, p, fmp, 0, 0, p, None, None) == -1
+    bad = (ctypes.c_int * 2)(0, 9)
+    assert L.fp8ds_scale_update(2, 16, p, p, p, ctypes.cast(bad, ctypes.c_void_p), 0, 0, p, None,
+                                None) == -3
+    # gemm: TT unsupported, bad op, small ld, misaligned ld, null C
+    args = dict(M=64, N=64, K=64)
+    g = lambda opa, opb, lda, ldb, ldc, C=p: L.fp8ds_gemm(opa, opb, 64, 64, 64, p, 0, lda, p, p, 0,
+                                                         ldb, p, C, 1, ldc, None, None)
+    assert g(1, 1, 64, 64, 64) == -6
+    assert g(2, 0, 64, 64, 64) == -3
+    assert g(0, 0, 32, 64, 64) == -2
+    assert g(0, 0, 72, 64, 64) == -4
+    assert g(0, 0, 64, 64, 64, C=None) == -1
+    assert g(0, 0, 64, 64, 66) == -4
+    assert args

@@ -1,0 +1,175 @@
+"""GPU parity: FP8 GEMM (NN, NT, TN) with FP32 accumulation, dequant to BF16 and
+the fused output amax, against the oracle."""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import delayed_scaling_gemm_amd as dsg  # noqa: E402
+from oracle import fp8 as ofp8  # noqa: E402
+from oracle import gemm as ogemm  # noqa: E402
+from tests.parity import bf16_bits, bf16_ulp, check_acc, check_bf16_out, f32_bits  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+LAYOUTS = [(dsg.OP_N, dsg.OP_N), (dsg.OP_N, dsg.OP_T), (dsg.OP_T, dsg.OP_N)]
+FMT_PAIRS = [(dsg.E4M3, dsg.E4M3), (dsg.E5M2, dsg.E4M3), (dsg.E4M3, dsg.E5M2),
+             (dsg.E5M2, dsg.E5M2)]
+
+
+def pad16(n):
+    return (n + 15) // 16 * 16
+
+
+def stored_shape(op, rows, cols):
+    """Stored array of op(X) = [rows x cols]."""
+    return (rows, cols) if op == dsg.OP_N else (cols, rows)
+
+
+def to_dev_padded(codes: np.ndarray):
+    """uint8 matrix to the device with its row length padded to 16 bytes; returns
+    (device tensor of the padded storage, leading dimension)."""
+    r, c = codes.shape
+    ld = pad16(max(c, 1))
+    buf = np.zeros((r, ld), dtype=np.uint8)
+    buf[:, :c] = codes
+    return torch.from_numpy(buf).to(DEV), ld
+
+
+def run_gemm(opa, opb, a_st, fa, b_st, fb, M, N, K, sa=1.0, sb=1.0, out=torch.float32):
+    A, lda = to_dev_padded(a_st)
+    B, ldb = to_dev_padded(b_st)
+    ldc = pad16(N)
+    C = torch.full((M, ldc), float("nan"), dtype=out, device=DEV)
+    s_a = torch.tensor([sa], dtype=torch.float32, device=DEV)
+    s_b = torch.tensor([sb], dtype=torch.float32, device=DEV)
+    am = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    dsg.fp8ds_gemm(opa, opb, M, N, K, A, fa, lda, s_a, B, fb, ldb, s_b, C, ldc, am)
+    torch.cuda.synchronize()
+    return C[:, :N].contiguous(), am.cpu().numpy().view(np.uint32)[0]
+
+
+def finite_codes(rng, shape, fmt, lo=0, hi=256):
+    c = rng.integers(lo, hi, shape).astype(np.uint8)
+    v = ofp8.decode(c, fmt)
+    c[~np.isfinite(v)] = 0x30
+    return c
+
+
+def int_codes(rng, shape, fmt):
+    r = 16 if fmt == dsg.E4M3 else 8
+    ints = rng.integers(-r, r + 1, shape)
+    return ofp8.encode(ints.astype(np.float32), fmt), ints
+
+
+@pytest.mark.parametrize("opa,opb", LAYOUTS)
+@pytest.mark.parametrize("fa,fb", FMT_PAIRS)
+@pytest.mark.parametrize("shape", [(300, 520, 384), (64, 64, 128), (1, 1, 1), (17, 33, 200),
+                                   (129, 257, 130)])
+def test_small_integers_exact(opa, opb, fa, fb, shape):
+    """Small integers are exact FP8 values and |sums| < 2^24: the FP32 output must
+    equal numpy's int64 matmul bit for bit."""
+    M, N, K = shape
+    rng = np.random.default_rng(M * 7 + N * 3 + K + 100 * opa + 10 * opb + fa * 5 + fb)
+    ca, ia = int_codes(rng, (M, K), fa)
+    cb, ib = int_codes(rng, (K, N), fb)
+    a_st = ca if opa == dsg.OP_N else np.ascontiguousarray(ca.T)
+    b_st = cb if opb == dsg.OP_N else np.ascontiguousarray(cb.T)
+    C, am = run_gemm(opa, opb, a_st, fa, b_st, fb, M, N, K)
+    exp = (ia @ ib).astype(np.float32)
+    got = C.cpu().numpy()
+    assert np.array_equal(got, exp), f"{np.count_nonzero(got != exp)} differ"
+    assert am == f32_bits(np.max(np.abs(exp)))
+
+
+@pytest.mark.parametrize("fa,fb", FMT_PAIRS)
+def test_code_pair_table(fa, fb):
+    """C[i, j] = value(i) * value(j) exactly for every pair of finite codes
+    (subnormals and mixed formats included)."""
+    K = 128
+    ta, tb = ofp8.decode_table(fa), ofp8.decode_table(fb)
+    ca = np.arange(256, dtype=np.uint8)
+    cb = np.arange(256, dtype=np.uint8)
+    ca[~np.isfinite(ta)] = 0
+    cb[~np.isfinite(tb)] = 0
+    for opa, opb in LAYOUTS:
+        A = np.zeros((256, K), np.uint8)
+        A[:, 0] = ca
+        B = np.zeros((K, 256), np.uint8)
+        B[0, :] = cb
+        a_st = A if opa == dsg.OP_N else np.ascontiguousarray(A.T)
+        b_st = B if opb == dsg.OP_N else np.ascontiguousarray(B.T)
+        C, _ = run_gemm(opa, opb, a_st, fa, b_st, fb, 256, 256, K)
+        exp = (np.where(np.isfinite(ta), ta, 0)[:, None] * np.where(np.isfinite(tb), tb, 0)[None, :])
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), exp)
+
+
+@pytest.mark.parametrize("opa,opb", LAYOUTS)
+@pytest.mark.parametrize("fa,fb", [(dsg.E4M3, dsg.E4M3), (dsg.E5M2, dsg.E4M3),
+                                   (dsg.E4M3, dsg.E5M2)])
+@pytest.mark.parametrize("shape", [(300, 520, 384), (257, 129, 1000), (520, 300, 2048)])
+def test_random_codes_within_tolerance(opa, opb, fa, fb, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M + N + K + opa * 11 + opb * 13 + fa * 17 + fb * 19)
+    # values of a realistic spread: codes drawn from the middle of the range
+    ca = finite_codes(rng, (M, K), fa, 0, 256)
+    cb = finite_codes(rng, (K, N), fb, 0, 256)
+    a_st = ca if opa == dsg.OP_N else np.ascontiguousarray(ca.T)
+    b_st = cb if opb == dsg.OP_N else np.ascontiguousarray(cb.T)
+    acc, sum_abs = ogemm.gemm_exact(a_st, fa, opa, b_st, fb, opb)
+    # FP32 accumulator check with unit scales
+    C, _ = run_gemm(opa, opb, a_st, fa, b_st, fb, M, N, K)
+    check_acc(C.cpu().numpy(), acc, sum_abs, "acc")
+    # BF16 output with scales, fused amax
+    sa, sb = np.float32(37.25), np.float32(0.0123)
+    Y, am = run_gemm(opa, opb, a_st, fa, b_st, fb, M, N, K, sa, sb, out=torch.bfloat16)
+    y_ref = ogemm.dequant_to_bf16(acc, sa, sb)
+    d = 1.0 / float(ogemm.dequant_scale(sa, sb))
+    yb = bf16_bits(Y)
+    check_bf16_out(yb, acc, sum_abs, y_ref, d, "bf16")
+    assert am == f32_bits(ogemm.output_amax(yb))  # bit-exact vs the GPU's own output
+    ref_am = float(ogemm.output_amax(y_ref))
+    got_am = float(np.array([am], np.uint32).view(np.float32)[0])
+    assert abs(got_am - ref_am) <= float(bf16_ulp(ref_am)) + 1e-5 * d * sum_abs.max()
+
+
+def test_zero_k_and_empty():
+    for opa, opb in LAYOUTS:
+        C, am = run_gemm(opa, opb, np.zeros((40 if opa == 0 else 0, 0), np.uint8).reshape(
+            (40, 0) if opa == 0 else (0, 40)), dsg.E4M3,
+            np.zeros((0, 24) if opb == 0 else (24, 0), np.uint8), dsg.E4M3, 40, 24, 0,
+            out=torch.bfloat16)
+        assert torch.all(C == 0).item() and am == 0
+    # M == 0: nothing to do, amax reset to 0
+    am = torch.full((1,), 7.0, dtype=torch.float32, device=DEV)
+    A = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    C = torch.zeros(16, dtype=torch.bfloat16, device=DEV)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    dsg.fp8ds_gemm(0, 0, 0, 16, 16, A, 0, 16, one, A, 0, 16, one, C, 16, am)
+    torch.cuda.synchronize()
+    assert am.item() == 0.0
+
+
+def test_batched_matches_oracle():
+    rng = np.random.default_rng(21)
+    Bn, M, N, K = 5, 96, 80, 160
+    ca = np.stack([finite_codes(rng, (M, K), dsg.E4M3) for _ in range(Bn)])
+    cb = np.stack([finite_codes(rng, (K, N), dsg.E4M3) for _ in range(Bn)])
+    sa = rng.uniform(0.5, 50, Bn).astype(np.float32)
+    sb = rng.uniform(0.5, 50, Bn).astype(np.float32)
+    A = torch.from_numpy(ca).to(DEV)
+    B = torch.from_numpy(cb).to(DEV)
+    C = torch.zeros((Bn, M, N), dtype=torch.bfloat16, device=DEV)
+    am = torch.zeros(Bn, dtype=torch.float32, device=DEV)
+    dsg.fp8ds_gemm_batched(0, 0, M, N, K, Bn, A, 0, K, M * K, torch.from_numpy(sa).to(DEV), B, 0, N,
+                           K * N, torch.from_numpy(sb).to(DEV), C, N, M * N, am)
+    torch.cuda.synchronize()
+    amn = am.cpu().numpy()
+    for b in range(Bn):
+        acc, sum_abs = ogemm.gemm_exact(ca[b], 0, 0, cb[b], 0, 0)
+        y_ref = ogemm.dequant_to_bf16(acc, sa[b], sb[b])
+        yb = bf16_bits(C[b])
+        check_bf16_out(yb, acc, sum_abs, y_ref, 1.0 / float(ogemm.dequant_scale(sa[b], sb[b])),
+                       f"batch {b}")
+        assert amn.view(np.uint32)[b] == f32_bits(ogemm.output_amax(yb))

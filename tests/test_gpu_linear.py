@@ -1,0 +1,142 @@
+"""GPU parity of whole Linear steps (casts, three GEMMs, scale update) against the
+oracle's training step: the tiny Linear over 4 steps, the decoder-layer
+projections' scale trajectories with the step-6 outlier, and the 4096-hidden
+Linear at full size in the benchmark's launch configuration (sampled rows)."""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import delayed_scaling_gemm_amd as dsg  # noqa: E402
+import workloads  # noqa: E402
+from delayed_scaling_gemm_amd.linear import DelayedScalingLinear  # noqa: E402
+from oracle import bf16 as obf16  # noqa: E402
+from oracle import fp8 as ofp8  # noqa: E402
+from oracle import gemm as ogemm  # noqa: E402
+from oracle import linear as olinear  # noqa: E402
+from oracle.scaling import ScalingState  # noqa: E402
+from tests.parity import bf16_bits, check_bf16_out, f32_bits  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def oracle_states(L):
+    return {"x": ScalingState(ofp8.E4M3, L), "w": ScalingState(ofp8.E4M3, L),
+            "dy": ScalingState(ofp8.E5M2, L)}
+
+
+def compare_state(lin, states, names=("x", "w", "dy")):
+    torch.cuda.synchronize()
+    h = lin.history.cpu().numpy()
+    c = lin.cursor.cpu().numpy()
+    s = lin.scale.cpu().numpy()
+    for i, nm in enumerate(names):
+        st = states[nm]
+        assert np.array_equal(h[i].view(np.uint32), st.history.view(np.uint32)), nm
+        assert c[i] == st.cursor and f32_bits(s[i]) == f32_bits(st.scale), (nm, s[i], st.scale)
+
+
+def compare_gemm(gpu_bf16, res: olinear.GemmResult, what):
+    yb = bf16_bits(gpu_bf16)
+    d = 1.0 / float(ogemm.dequant_scale(res.scale_a, res.scale_b))
+    check_bf16_out(yb, res.acc, res.sum_abs, res.y_bits, d, what)
+    return yb
+
+
+def test_tiny_linear_four_steps():
+    lin = DelayedScalingLinear(hist_len=16, algo=dsg.ALGO_MAX, margin=0)
+    states = oracle_states(16)
+    for step in range(4):
+        x, w, dy = workloads.tiny_linear_step(step)
+        tx, tw, tdy = (torch.from_numpy(a).to(DEV) for a in (x, w, dy))
+        out = lin.step(tx, tw, tdy)
+        torch.cuda.synchronize()
+        ref = olinear.train_step(x, w, dy, states, 0, 0)
+        for key, ck, i in (("xq", "cast_x", 0), ("wq", "cast_w", 1), ("dyq", "cast_dy", 2)):
+            c = ref[ck]
+            assert np.array_equal(out[key].cpu().numpy().ravel(), c.codes.ravel()), (step, key)
+            assert f32_bits(lin.amax[i].item()) == f32_bits(c.amax)
+            assert f32_bits(lin.scale_used[i].item()) == f32_bits(c.scale_used)
+            assert lin.sat[i].item() == c.sat
+        yb = compare_gemm(out["y"], ref["y"], f"y step {step}")
+        assert f32_bits(lin.amax_y.item()) == f32_bits(ogemm.output_amax(yb))
+        compare_gemm(out["dx"], ref["dx"], f"dx step {step}")
+        compare_gemm(out["dw"], ref["dw"], f"dw step {step}")
+        compare_state(lin, states)
+
+
+@pytest.mark.parametrize("algo", [dsg.ALGO_MAX, dsg.ALGO_MOST_RECENT])
+def test_decoder_projection_outlier_trajectory(algo):
+    """10 steps of the k_proj Linear with drifting activations and the 50x batch at
+    step 6 (first 512 token rows): every byte of the casts, every scale, history
+    and cursor bit-exact; all three GEMMs within tolerance."""
+    M = 512
+    lin = DelayedScalingLinear(hist_len=16, algo=algo, margin=0)
+    states = oracle_states(16)
+    for step in range(10):
+        xb, wb, dyb = workloads.llama_tensors("k_proj", step, m=M)
+        out = lin.step(dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb))
+        x, w, dy = obf16.widen(xb), obf16.widen(wb), obf16.widen(dyb)
+        ref = olinear.train_step(x, w, dy, states, algo, 0)
+        torch.cuda.synchronize()
+        for key, ck in (("xq", "cast_x"), ("wq", "cast_w"), ("dyq", "cast_dy")):
+            assert np.array_equal(out[key].cpu().numpy(), ref[ck].codes), (step, key)
+        assert lin.sat[0].item() == ref["cast_x"].sat
+        compare_gemm(out["y"], ref["y"], f"y {step}")
+        compare_gemm(out["dx"], ref["dx"], f"dx {step}")
+        compare_gemm(out["dw"], ref["dw"], f"dw {step}")
+        compare_state(lin, states)
+
+
+def _sampled_rows_check(gpu_out, a_codes, fa, opa, b_codes, fb, opb, sa, sb, rows, what):
+    """Oracle GEMM on a sample of output rows only."""
+    a_rows = a_codes[rows] if opa == dsg.OP_N else a_codes[:, rows].T
+    acc, sum_abs = ogemm.gemm_exact(np.ascontiguousarray(a_rows), fa, 0, b_codes, fb, opb)
+    y_ref = ogemm.dequant_to_bf16(acc, sa, sb)
+    yb = bf16_bits(gpu_out[torch.from_numpy(rows).to(DEV)])
+    d = 1.0 / float(ogemm.dequant_scale(sa, sb))
+    check_bf16_out(yb, acc, sum_abs, y_ref, d, what)
+
+
+def test_fwd_bwd_4096_full_size_sampled():
+    """The M=16384, 4096-hidden Linear at full size, launched exactly as the
+    benchmark launches it: all cast bytes on a sample, amax and saturation exact,
+    64 sampled rows of each GEMM output against the oracle, output amax exact."""
+    xb, wb, dyb = workloads.fwd_bwd_4096()
+    print("[fwd_bwd_4096] inputs ready", flush=True)
+    lin = DelayedScalingLinear(hist_len=16)
+    # step 0 runs at scale 1.0; step 1 at the scales derived from step 0
+    states = oracle_states(16)
+    for step in range(2):
+        out = lin.step(dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb))
+        torch.cuda.synchronize()
+        xq, wq, dyq = (out[k].cpu().numpy() for k in ("xq", "wq", "dyq"))
+        rng = np.random.default_rng(step)
+        for name, st, bits, q in (("x", states["x"], xb, xq), ("w", states["w"], wb, wq),
+                                  ("dy", states["dy"], dyb, dyq)):
+            flat = bits.ravel()
+            pos = rng.choice(flat.size, 1 << 18, replace=False)
+            codes, _ = ofp8.cast(obf16.widen(flat[pos]), st.scale, st.fmt)
+            assert np.array_equal(q.ravel()[pos], codes), (step, name)
+        i_x, i_w, i_dy = 0, 1, 2
+        su = lin.scale_used.cpu().numpy()
+        assert f32_bits(su[i_x]) == f32_bits(states["x"].scale)
+        rows = np.sort(rng.choice(16384, 64, replace=False))
+        _sampled_rows_check(out["y"], xq, 0, 0, wq, 0, 0, su[i_x], su[i_w], rows, "y")
+        _sampled_rows_check(out["dx"], dyq, 1, 0, wq, 0, 1, su[i_dy], su[i_w], rows, "dx")
+        rows_k = np.sort(rng.choice(4096, 64, replace=False))
+        _sampled_rows_check(out["dw"], xq, 0, 1, dyq, 1, 0, su[i_x], su[i_dy], rows_k, "dw")
+        yb = bf16_bits(out["y"])
+        assert f32_bits(lin.amax_y.item()) == f32_bits(ogemm.output_amax(yb))
+        # advance the oracle's scaling state with exact amaxes of the full tensors
+        from oracle import amax as oamax
+        for name, bits in (("x", xb), ("w", wb), ("dy", dyb)):
+            states[name].update(oamax.amax(obf16.widen(bits)), 0, 0)
+        compare_state(lin, states)
+        print(f"[fwd_bwd_4096] step {step} ok", flush=True)
