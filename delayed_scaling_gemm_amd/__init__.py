@@ -23,6 +23,7 @@ E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
 OP_N, OP_T = 0, 1
+MMA_EXACT, MMA_FP8 = 0, 1
 
 FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
 
@@ -57,10 +58,10 @@ def _declare(lib):
     lib.fp8ds_scale_update.argtypes = [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp]
     lib.fp8ds_gemm.restype = i32
     lib.fp8ds_gemm.argtypes = [i32, i32, i64, i64, i64, vp, i32, i64, vp, vp, i32, i64, vp, vp, i32,
-                               i64, vp, vp]
+                               i64, vp, i32, vp]
     lib.fp8ds_gemm_batched.restype = i32
     lib.fp8ds_gemm_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i32, i64, i64, vp, vp, i32,
-                                       i64, i64, vp, vp, i32, i64, i64, vp, vp]
+                                       i64, i64, vp, vp, i32, i64, i64, vp, i32, vp]
     return lib
 
 
@@ -150,19 +151,20 @@ def fp8ds_scale_update(history, cursor, amax, fmts, algo, margin, scale, scale_i
 
 
 def fp8ds_gemm(opa, opb, M, N, K, a, fa, lda, scale_a, b, fb, ldb, scale_b, c, ldc, amax_c=None,
-               stream=None):
+               stream=None, mma=MMA_EXACT):
     """``c = dequant(op(a) @ op(b))`` with FP32 accumulation; ``c`` is bf16 or fp32."""
     _check(lib().fp8ds_gemm(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_a), _ptr(b), fb, ldb,
-                            _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c),
+                            _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c), mma,
                             _stream(stream)))
 
 
 def fp8ds_gemm_batched(opa, opb, M, N, K, batch, a, fa, lda, stride_a, scale_a, b, fb, ldb,
-                       stride_b, scale_b, c, ldc, stride_c, amax_c=None, stream=None):
+                       stride_b, scale_b, c, ldc, stride_c, amax_c=None, stream=None,
+                       mma=MMA_EXACT):
     """``batch`` GEMMs of one shape with per-problem scales and output amax."""
     _check(lib().fp8ds_gemm_batched(opa, opb, M, N, K, batch, _ptr(a), fa, lda, stride_a,
                                     _ptr(scale_a), _ptr(b), fb, ldb, stride_b, _ptr(scale_b),
-                                    _ptr(c), _dtype_code(c), ldc, stride_c, _ptr(amax_c),
+                                    _ptr(c), _dtype_code(c), ldc, stride_c, _ptr(amax_c), mma,
                                     _stream(stream)))
 
 

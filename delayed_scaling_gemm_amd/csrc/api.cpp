@@ -176,7 +176,9 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
                        int64_t stride_a, const float* scale_a, const uint8_t* B, fp8ds_format fb,
                        int64_t ldb, int64_t stride_b, const float* scale_b, void* C,
                        fp8ds_dtype ct, int64_t ldc, int64_t stride_c, float* amax_c,
-                       hipStream_t stream) {
+                       fp8ds_mma mma, hipStream_t stream) {
+  if (mma != FP8DS_MMA_EXACT && mma != FP8DS_MMA_FP8)
+    return fail(FP8DS_ERR_ENUM, "%s: bad mma %d", who, (int)mma);
   if ((opa != FP8DS_OP_N && opa != FP8DS_OP_T) || (opb != FP8DS_OP_N && opb != FP8DS_OP_T))
     return fail(FP8DS_ERR_ENUM, "%s: bad op", who);
   if (opa == FP8DS_OP_T && opb == FP8DS_OP_T)
@@ -221,7 +223,8 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
     p.B = B; p.fb = (int)fb; p.ldb = ldb; p.scale_b = scale_b;
     p.C = C; p.out_bf16 = ct == FP8DS_BF16; p.ldc = ldc; p.amax_c = amax_c;
     p.batch = batch; p.stride_a = stride_a; p.stride_b = stride_b; p.stride_c = stride_c;
-    e = fp8ds::launch_gemm(p, num_cus(), stream);
+    e = mma == FP8DS_MMA_EXACT ? fp8ds::launch_gemm_exact(p, num_cus(), stream)
+                               : fp8ds::launch_gemm_fp8(p, num_cus(), stream);
   }
   return hip_status(e, who);
 }
@@ -229,18 +232,19 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
 int fp8ds_gemm(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                fp8ds_format fa, int64_t lda, const float* scale_a, const uint8_t* B,
                fp8ds_format fb, int64_t ldb, const float* scale_b, void* C, fp8ds_dtype ct,
-               int64_t ldc, float* amax_c, hipStream_t stream) {
+               int64_t ldc, float* amax_c, fp8ds_mma mma, hipStream_t stream) {
   return gemm_common("fp8ds_gemm", opa, opb, M, N, K, 1, A, fa, lda, 0, scale_a, B, fb, ldb, 0,
-                     scale_b, C, ct, ldc, 0, amax_c, stream);
+                     scale_b, C, ct, ldc, 0, amax_c, mma, stream);
 }
 
 int fp8ds_gemm_batched(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K, int64_t batch,
                        const uint8_t* A, fp8ds_format fa, int64_t lda, int64_t stride_a,
                        const float* scale_a, const uint8_t* B, fp8ds_format fb, int64_t ldb,
                        int64_t stride_b, const float* scale_b, void* C, fp8ds_dtype ct,
-                       int64_t ldc, int64_t stride_c, float* amax_c, hipStream_t stream) {
+                       int64_t ldc, int64_t stride_c, float* amax_c, fp8ds_mma mma,
+                       hipStream_t stream) {
   return gemm_common("fp8ds_gemm_batched", opa, opb, M, N, K, batch, A, fa, lda, stride_a, scale_a,
-                     B, fb, ldb, stride_b, scale_b, C, ct, ldc, stride_c, amax_c, stream);
+                     B, fb, ldb, stride_b, scale_b, C, ct, ldc, stride_c, amax_c, mma, stream);
 }
 
 }  // extern "C"

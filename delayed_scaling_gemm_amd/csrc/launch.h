@@ -51,6 +51,9 @@ struct GemmProblem {
   int64_t batch;
   int64_t stride_a, stride_b, stride_c;  // bytes, bytes, elements
 };
-hipError_t launch_gemm(const GemmProblem& p, int num_cus, hipStream_t stream);
+// EXACT datapath: FP8 widened to F16, F16 MFMA, FP32 sums.
+hipError_t launch_gemm_exact(const GemmProblem& p, int num_cus, hipStream_t stream);
+// FP8 datapath: native FP8 MFMA (hardware summation precision).
+hipError_t launch_gemm_fp8(const GemmProblem& p, int num_cus, hipStream_t stream);
 
 }  // namespace fp8ds

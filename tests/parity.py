@@ -21,22 +21,23 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return np.where(a > 0, np.ldexp(1.0, e - 7), 2.0**-133)
 
 
-def check_acc(acc_gpu: np.ndarray, acc_exact: np.ndarray, sum_abs: np.ndarray, what=""):
-    """|acc_gpu - acc_exact| <= 1e-5 * sum|ab| element by element."""
+def check_acc(acc_gpu: np.ndarray, acc_exact: np.ndarray, sum_abs: np.ndarray, what="",
+              rel=ACC_REL):
+    """|acc_gpu - acc_exact| <= rel * sum|ab| element by element (rel = 1e-5 by default)."""
     err = np.abs(acc_gpu.astype(np.float64) - acc_exact)
-    bound = ACC_REL * sum_abs
+    bound = rel * sum_abs
     bad = err > bound
     assert not bad.any(), (f"{what}: {bad.sum()} elements out of tolerance; worst "
                            f"err {err[bad].max():.3e} bound {bound[bad].min():.3e}")
 
 
 def check_bf16_out(y_gpu_bits: np.ndarray, acc_exact: np.ndarray, sum_abs: np.ndarray,
-                   y_ref_bits: np.ndarray, d: float, what=""):
-    """|y_gpu - y_ref| <= ulp_bf16(y_ref) + 1e-5 * d * sum|ab|."""
+                   y_ref_bits: np.ndarray, d: float, what="", rel=ACC_REL):
+    """|y_gpu - y_ref| <= ulp_bf16(y_ref) + rel * d * sum|ab| (rel = 1e-5 by default)."""
     yg = obf16.widen(y_gpu_bits).astype(np.float64)
     yr = obf16.widen(y_ref_bits).astype(np.float64)
     err = np.abs(yg - yr)
-    bound = bf16_ulp(yr) + ACC_REL * d * sum_abs
+    bound = bf16_ulp(yr) + rel * d * sum_abs
     bad = err > bound
     assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outputs out of tolerance; "
                            f"e.g. gpu {yg[bad][:3]} ref {yr[bad][:3]}")

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(dsg.LIB_PATH)
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert dsg.abi_version() == 1
+    assert dsg.abi_version() == 2
 
 
 def test_status_strings():
@@ -76,12 +76,14 @@ def test_validation_errors_without_gpu():
                                 None) == -3
     # gemm: TT unsupported, bad op, small ld, misaligned ld, null C
     args = dict(M=64, N=64, K=64)
-    g = lambda opa, opb, lda, ldb, ldc, C=p: L.fp8ds_gemm(opa, opb, 64, 64, 64, p, 0, lda, p, p, 0,
-                                                         ldb, p, C, 1, ldc, None, None)
+    g = lambda opa, opb, lda, ldb, ldc, C=p, mma=0: L.fp8ds_gemm(opa, opb, 64, 64, 64, p, 0, lda, p,
+                                                                p, 0, ldb, p, C, 1, ldc, None, mma,
+                                                                None)
     assert g(1, 1, 64, 64, 64) == -6
     assert g(2, 0, 64, 64, 64) == -3
     assert g(0, 0, 32, 64, 64) == -2
     assert g(0, 0, 72, 64, 64) == -4
     assert g(0, 0, 64, 64, 64, C=None) == -1
+    assert g(0, 0, 64, 64, 64, mma=2) == -3
     assert g(0, 0, 64, 64, 66) == -4
     assert args
