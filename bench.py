@@ -115,14 +115,15 @@ def main():
         bufs = lin._bufs
         if "xq" not in bufs:
             lin.step(x, w, dy)  # allocates the output buffers once
-        xq, wq, y, dyq, dx, dw = (bufs[k] for k in ("xq", "wq", "y", "dyq", "dx", "dw"))
+        xq, wq, wqt, y, dyq, dx, dw = (bufs[k] for k in ("xq", "wq", "wqt", "y", "dyq", "dx",
+                                                           "dw"))
         s, su, am, sat = lin.scale, lin.scale_used, lin.amax, lin.sat
         ev[0].record(stream)
         fp8ds_cast(x, E4M3, s[0:1], xq, None, su[0:1], am[0:1], sat[0:1])
         ev[1].record(stream)
-        fp8ds_cast(w, E4M3, s[1:2], wq, None, su[1:2], am[1:2], sat[1:2])
+        fp8ds_cast(w, E4M3, s[1:2], wq, wqt, su[1:2], am[1:2], sat[1:2])
         ev[2].record(stream)
-        fp8ds_gemm(OP_N, OP_N, M, N, K, xq, E4M3, K, su[0:1], wq, E4M3, N, su[1:2], y, N,
+        fp8ds_gemm(OP_N, OP_T, M, N, K, xq, E4M3, K, su[0:1], wqt, E4M3, K, su[1:2], y, N,
                    lin.amax_y)
         ev[3].record(stream)
         fp8ds_cast(dy, E5M2, s[2:3], dyq, None, su[2:3], am[2:3], sat[2:3])

@@ -107,6 +107,9 @@ int fp8ds_cast(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_
     if (!aligned16(x) || !aligned16(q) || (q_t && !aligned16(q_t)))
       return fail(FP8DS_ERR_ALIGN, "fp8ds_cast: x, q and q_t must be 16-byte aligned");
   }
+  if (q_t && (rows + 127) / 128 > 65535)
+    return fail(FP8DS_ERR_SHAPE, "fp8ds_cast: a transposed copy supports at most %d rows",
+                65535 * 128);
   hipError_t e = fp8ds::launch_prologue(1, scale, scale_used, amax, sat_count, stream);
   if (e == hipSuccess && n > 0) {
     if (q_t)

@@ -183,10 +183,31 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs p) {
 }
 
 // ------------------------------------------------------------------ cast + transposed copy
-// Tiles of 64 x 64 elements: each thread converts 16 consecutive elements of one
-// row (coalesced read, 16-byte store to q), parks the codes in LDS, and after a
-// barrier writes 16 consecutive rows of one column to q_t.  Partial tiles take
-// element-wise guarded paths.
+// A 128 x 128 tile per workgroup.  Full tiles of suitably aligned tensors take
+// the vector path:
+//   * each thread converts four 16-element row pieces (16-byte loads), stores the
+//     16 codes of each to q with one 16-byte store and parks them in an LDS tile
+//     of 128-byte rows;
+//   * after a barrier each thread reads a 16-row x 4-column block of codes as 16
+//     dwords (32 lanes read one whole LDS row: no bank conflicts), transposes it
+//     in registers with byte permutes and stores four 16-byte pieces of q_t
+//     (16 consecutive rows of one input column each).
+// Other tiles (ragged edges, unaligned shapes) convert element by element.
+
+__device__ __forceinline__ void transpose4x4_b(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t i3,
+                                               uint32_t& o0, uint32_t& o1, uint32_t& o2,
+                                               uint32_t& o3) {
+  // __builtin_amdgcn_perm(hi, lo, sel): byte i of the result is byte sel.byte_i of
+  // hi:lo (selector 0..3 = lo bytes, 4..7 = hi bytes); out[b] = byte b of i0..i3.
+  const uint32_t t0 = __builtin_amdgcn_perm(i1, i0, 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(i1, i0, 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(i3, i2, 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(i3, i2, 0x07030602u);
+  o0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  o1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  o2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
 
 template <bool BF16, int FMT>
 __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restrict__ xp,
@@ -196,52 +217,97 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restr
                                                              uint8_t* __restrict__ qt,
                                                              uint32_t* __restrict__ g_amax,
                                                              unsigned long long* __restrict__ g_sat) {
-  __shared__ uint8_t tile[64][64 + 4];
+  constexpr int T = 128;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[T * T];
   __shared__ uint32_t red[8];
   const float s = scale[0];
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
-  const int tr = threadIdx.x >> 2;         // row within tile
-  const int tc = (threadIdx.x & 3) * 16;   // first column within tile
-  const int64_t r = r0 + tr;
+  const int64_t r0 = (int64_t)blockIdx.y * T;
+  const int64_t c0 = (int64_t)blockIdx.x * T;
+  const int tid = threadIdx.x;
   uint32_t amax = 0, sat = 0;
-  uint8_t codes[16];
+  // vector path: whole tile inside, 16-element pieces aligned for 16-byte
+  // accesses in x, q and q_t
+  const bool vec = (r0 + T <= rows) && (c0 + T <= cols) && (cols % 16 == 0) && (rows % 16 == 0);
+  if (vec) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t c = c0 + tc + i;
-    uint32_t code = 0;
-    if (r < rows && c < cols) {
-      float v;
+    for (int i = 0; i < 4; ++i) {
+      const int piece = tid + 256 * i;
+      const int r = piece >> 3, cp = (piece & 7) * 16;
+      const int64_t off = (r0 + r) * cols + c0 + cp;
+      u32x4 codes;
       if constexpr (BF16) {
-        uint32_t bits = static_cast<const uint16_t*>(xp)[r * cols + c];
-        amax = max(amax, (bits & 0x7FFFu) << 16);
-        v = __uint_as_float(bits << 16) * s;
+        const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xp) + off);
+        const u32x4 v0 = src[0], v1 = src[1];
+        const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        u16x2 amax2 = {0, 0};
+        codes = cast16_bf16<FMT>(d, s, amax2, sat, g_sat != nullptr);
+        amax = max(amax, ((uint32_t)max(amax2.x, amax2.y)) << 16);
       } else {
-        uint32_t bits = static_cast<const uint32_t*>(xp)[r * cols + c];
-        amax = max(amax, bits & 0x7FFFFFFFu);
-        v = __uint_as_float(bits) * s;
+        const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(xp) + off);
+        uint32_t d[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4 v = src[k];
+          d[4 * k] = v.x; d[4 * k + 1] = v.y; d[4 * k + 2] = v.z; d[4 * k + 3] = v.w;
+        }
+        codes = cast16_f32<FMT>(d, s, amax, sat, g_sat != nullptr);
       }
-      code = encode_fp8<FMT>(v);
-      if (g_sat) sat += (uint32_t)(fabsf(v) > FmtTraits<FMT>::kMax);
+      *reinterpret_cast<u32x4*>(q + off) = codes;
+      *reinterpret_cast<u32x4*>(tile + r * T + cp) = codes;
     }
-    codes[i] = (uint8_t)code;
-    tile[tr][tc + i] = (uint8_t)code;
-  }
-  if (r < rows) {
+    __syncthreads();
+    {
+      const int cb = tid & 31;  // 4-column block
+      const int rb = tid >> 5;  // 16-row block
+      uint32_t w[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+      for (int j = 0; j < 16; ++j)
+        w[j] = *reinterpret_cast<const uint32_t*>(tile + (rb * 16 + j) * T + cb * 4);
+      uint32_t col[4][4];  // col[c][g]: rows 4g..4g+3 of column 4 cb + c
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        transpose4x4_b(w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3], col[0][g], col[1][g],
+                       col[2][g], col[3][g]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int64_t oc = c0 + cb * 4 + c;
+        *reinterpret_cast<u32x4*>(qt + oc * rows + r0 + rb * 16) =
+            u32x4{col[c][0], col[c][1], col[c][2], col[c][3]};
+      }
+    }
+  } else {
+    const int tr = tid >> 1;         // row within the tile
+    const int tc = (tid & 1) * 64;   // first of this thread's 64 columns
+    const int64_t r = r0 + tr;
+    for (int i = 0; i < 64; ++i) {
       const int64_t c = c0 + tc + i;
-      if (c < cols) q[r * cols + c] = codes[i];
+      uint32_t code = 0;
+      if (r < rows && c < cols) {
+        float v;
+        if constexpr (BF16) {
+          const uint32_t bits = static_cast<const uint16_t*>(xp)[r * cols + c];
+          amax = max(amax, (bits & 0x7FFFu) << 16);
+          v = __uint_as_float(bits << 16) * s;
+        } else {
+          const uint32_t bits = static_cast<const uint32_t*>(xp)[r * cols + c];
+          amax = max(amax, bits & 0x7FFFFFFFu);
+          v = __uint_as_float(bits) * s;
+        }
+        code = encode_fp8<FMT>(v);
+        if (g_sat) sat += (uint32_t)(fabsf(v) > FmtTraits<FMT>::kMax);
+        q[r * cols + c] = (uint8_t)code;
+      }
+      tile[tr * T + tc + i] = (uint8_t)code;
     }
-  }
-  __syncthreads();
-  // transposed: thread writes column (c0 + tr), rows r0 + tc .. +15
-  const int64_t oc = c0 + tr;
-  if (oc < cols) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t orow = r0 + tc + i;
-      if (orow < rows) qt[oc * rows + orow] = tile[tc + i][tr];
+    __syncthreads();
+    const int oc_l = tid >> 1;       // column within the tile
+    const int orr = (tid & 1) * 64;  // first of this thread's 64 rows
+    const int64_t oc = c0 + oc_l;
+    if (oc < cols) {
+      for (int i = 0; i < 64; ++i) {
+        const int64_t orow = r0 + orr + i;
+        if (orow < rows) qt[oc * rows + orow] = tile[(orr + i) * T + oc_l];
+      }
     }
   }
   block_commit_amax_sat(amax, sat, g_amax, g_sat, red);
@@ -302,7 +368,7 @@ hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64
 hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
                                  const float* scale, uint8_t* q, uint8_t* qt, float* amax,
                                  uint64_t* sat, hipStream_t stream) {
-  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
   uint32_t* am = reinterpret_cast<uint32_t*>(amax);
   unsigned long long* st = reinterpret_cast<unsigned long long*>(sat);
   if (bf16) {

@@ -2,8 +2,8 @@
 
 Host-side orchestration only (every arithmetic step runs in the HIP library):
 
-  fwd:  cast X (E4M3), cast W (E4M3)          -> Xq, Wq, amax_X, amax_W, scale snapshots
-        Y  = Xq . Wq         (NN)             -> BF16 Y + amax_Y
+  fwd:  cast X (E4M3), cast W (E4M3)          -> Xq, Wq (+ Wq^T), amax_X, amax_W, snapshots
+        Y  = Xq . Wq         (NT on Wq^T)     -> BF16 Y + amax_Y
   bwd:  cast dY (E5M2)                        -> dYq, amax_dY
         dX = dYq . Wq^T      (NT)             -> BF16 dX
         dW = Xq^T . dYq      (TN)             -> BF16 dW
@@ -13,8 +13,10 @@ This is the HYBRID recipe ("LLM FP8 微调上线生产实战" §核心原理: E4
 tensors, E5M2 for gradients) with delayed scaling: each cast uses the scale that
 the previous steps' amax history produced, and the GEMMs use the snapshot of the
 scale their operands were cast with ("FP8 混合精度训练工程实践" §四 动态缩放).
-W is stored [in, out], so the forward product is NN.  The backward products
-reuse the forward FP8 bytes of X and W.
+W is stored [in, out].  The cast of W also writes the transposed bytes Wq^T
+[out, in], so the forward product runs with both operands K-contiguous (the
+GEMM's fastest layout); the backward products reuse the forward FP8 bytes of X
+and W.
 
 Everything stays on the device and on one stream: there is no host
 synchronisation inside a step.
@@ -69,15 +71,17 @@ class DelayedScalingLinear:
         u8 = torch.uint8
         xq = self._buf("xq", (M, K), u8)
         wq = self._buf("wq", (K, N), u8)
+        wqt = self._buf("wqt", (N, K), u8)
         y = self._buf("y", (M, N), torch.bfloat16)
         s, su, am, sat = self.scale, self.scale_used, self.amax, self.sat
         fp8ds_cast(x, self.fmts[X], s[X:X + 1], xq, None, su[X:X + 1], am[X:X + 1], sat[X:X + 1],
                    stream)
-        fp8ds_cast(w, self.fmts[W], s[W:W + 1], wq, None, su[W:W + 1], am[W:W + 1], sat[W:W + 1],
+        fp8ds_cast(w, self.fmts[W], s[W:W + 1], wq, wqt, su[W:W + 1], am[W:W + 1], sat[W:W + 1],
                    stream)
-        fp8ds_gemm(OP_N, OP_N, M, N, K, xq, self.fmts[X], K, su[X:X + 1], wq, self.fmts[W], N,
+        # Y[M, N] = Xq[M, K] . Wq[K, N], with Wq^T stored [N, K] -> op T
+        fp8ds_gemm(OP_N, OP_T, M, N, K, xq, self.fmts[X], K, su[X:X + 1], wqt, self.fmts[W], K,
                    su[W:W + 1], y, N, self.amax_y, stream)
-        out = {"xq": xq, "wq": wq, "y": y}
+        out = {"xq": xq, "wq": wq, "wqt": wqt, "y": y}
         n_upd = 2
         if dy is not None:
             assert tuple(dy.shape) == (M, N)

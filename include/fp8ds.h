@@ -128,7 +128,8 @@ int fp8ds_amax(const void* x, fp8ds_dtype xt, int64_t n, float* amax, hipStream_
  *   q          device, rows*cols bytes, row-major, 16-byte aligned.
  *   q_t        device or NULL: if non-NULL also receives the transposed copy,
  *              [cols x rows] row-major (q_t[c*rows + r] == q[r*cols + c]), for GEMM
- *              operands the caller wants K-contiguous.  16-byte aligned.
+ *              operands the caller wants K-contiguous.  16-byte aligned; rows at
+ *              most 65535 * 128 (else FP8DS_ERR_SHAPE).
  *   scale_used device or NULL: receives a copy of *scale -- the snapshot the FP8
  *              bytes were made with.  GEMMs must be given this snapshot, because
  *              fp8ds_scale_update overwrites *scale for the next step.

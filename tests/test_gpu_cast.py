@@ -134,19 +134,27 @@ def test_standalone_amax():
             assert got == f32_bits(oamax.amax(xr)), (x32[:4], bf16)
 
 
-@pytest.mark.parametrize("shape", [(130, 70), (64, 64), (1, 100), (100, 1), (257, 513)])
-def test_cast_with_transposed_copy(shape):
+@pytest.mark.parametrize("shape", [(130, 70), (64, 64), (1, 100), (100, 1), (257, 513),
+                                   (256, 384), (384, 128), (272, 400), (128, 2048), (1024, 1040)])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_cast_with_transposed_copy(shape, bf16):
+    """q and its transpose q_t: full 128 x 128 tiles of aligned shapes take the
+    vector path, other tiles the element-wise path; both must match the oracle."""
     rows, cols = shape
-    rng = np.random.default_rng(rows * 1000 + cols)
+    rng = np.random.default_rng(rows * 1000 + cols + bf16)
     x32 = (rng.standard_normal(rows * cols) * 200).astype(np.float32)
-    bits = workloads.to_bf16_bits(x32)
-    xr = obf16.widen(bits)
+    x32[rng.choice(x32.size, min(5, x32.size), replace=False)] = 7.0e4  # saturate both formats
+    if bf16:
+        bits = workloads.to_bf16_bits(x32)
+        xd, xr = dev_bf16(bits), obf16.widen(bits)
+    else:
+        xd, xr = dev_f32(x32), x32
     for fmt in FMTS:
-        q, qt, su, am, sat = run_cast(dev_bf16(bits), fmt, 1.5, rows, cols, transpose=True)
+        q, qt, su, am, sat = run_cast(xd, fmt, 1.5, rows, cols, transpose=True)
         codes, oa, osat = oracle_cast(xr, fmt, 1.5)
         assert np.array_equal(q, codes)
         assert np.array_equal(qt.reshape(cols, rows), codes.reshape(rows, cols).T)
-        assert am == oa and sat == osat
+        assert am == oa and sat == osat and su == 1.5
 
 
 def test_cast_batched():
