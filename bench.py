@@ -1,25 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the FP8 delayed-scaling Linear on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input:
+One step = one pass of the whole hot path over one batch of synthetic input,
 the fwd+bwd Linear at 4096 hidden with M = 16384 tokens (X, W, dY bf16; HYBRID
-recipe E4M3 forward / E5M2 gradients; amax history 16, window max, margin 0):
+recipe: E4M3 forward, E5M2 gradients; amax history 16, window max, margin 0):
 
-  cast X, cast W (fused amax)  ->  Y = Xq Wq (NN)  ->  cast dY  ->
-  dX = dYq Wq^T (NT)  ->  dW = Xq^T dYq (TN)  ->  scale update of 3 histories
+  cast X (fused amax)  ->  cast W (+ transposed bytes)  ->  Y = Xq Wq  ->
+  cast dY  ->  dX = dYq Wq^T  ->  dW = Xq^T dYq  ->  scale update of 3 histories
 
-`value` is the step's FP8 GEMM work (3 x 2 M N K flop) divided by the measured
-time of the whole step (casts and scale update included), in TFLOP/s.  Inputs
-are resident in HBM before timing; four input sets are rotated so that the
-256 MB Infinity Cache cannot hold a step's working set.  Per-kernel times come
-from HIP events recorded on the stream the kernels are launched on.
+`value` is the step's GEMM work (3 x 2 M N K flop) over the measured time of the
+whole step (casts and scale update included), in TFLOP/s.  Inputs are resident
+in HBM before timing; four input sets are rotated so that the 256 MB Infinity
+Cache cannot hold a step's working set.  Per-kernel times come from HIP events
+recorded between the launches on the stream the library launches on.
 
-Prints one JSON line.  `--gpus N` with N > 1 is not supported (single-GPU build).
+Prints one JSON line.  `--gpus N` with N > 1 is refused: this build measures
+one GPU.  `--copy-calib` only runs device copies of known size (the reference
+for the HBM byte counters, see profiles/).
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,9 +35,14 @@ sys.path.insert(0, ROOT)
 
 M_TOK, K_IN, N_OUT = 16384, 4096, 4096
 HIST_LEN = 16
-PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
-PEAK_HBM_GBPS = 8000.0    # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense F16 MFMA (the instruction of the exact datapath)
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 N_SETS = 4
+CPU_SAMPLE_ROWS = 8192
+KERNEL_SOURCES = ["delayed_scaling_gemm_amd/csrc/gemm_kernel.h",
+                  "delayed_scaling_gemm_amd/csrc/device_common.h"]
+TRAFFIC_FILE = "profiles/gemm_linear_4096_m16384_traffic.txt"
 
 
 def parse():
@@ -44,10 +52,39 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stress", action="store_true")
+    ap.add_argument("--no-fp8-path", action="store_true",
+                    help="skip the context timing of the FP8-MFMA datapath")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB and exit")
     return ap.parse_args()
 
 
-def cpu_baseline(xb, wb, dyb, rows=1024):
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when there is none or it was taken on another version of the kernel source."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    key = f"{kernel}_hbm_bytes_per_launch"
+    return float(fields[key]) if key in fields else None
+
+
+def cpu_baseline(xb, wb, dyb, rows=CPU_SAMPLE_ROWS):
     """The oracle's training step on a row sample of the same workload (CPU)."""
     from oracle import bf16 as obf16
     from oracle import fp8 as ofp8
@@ -63,29 +100,93 @@ def cpu_baseline(xb, wb, dyb, rows=1024):
     olinear.train_step(x, w, dy, states, 0, 0)
     dt = time.perf_counter() - t0
     flops = 3 * 2 * rows * K_IN * N_OUT
+    try:
+        import threadpoolctl
+        blas = max((p.get("num_threads", 0) for p in threadpoolctl.threadpool_info()), default=0)
+    except Exception:  # threadpoolctl is optional
+        blas = 0
+    cores = len(os.sched_getaffinity(0))
     return {
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": len(os.sched_getaffinity(0)),
+        "cores": max(blas, 1) if blas else cores,
         "kind": "oracle",
-        "sample": f"one oracle fwd+bwd step on the first {rows} of {M_TOK} token rows "
-                  f"(casts of X[{rows}x{K_IN}], W[{K_IN}x{N_OUT}], dY[{rows}x{N_OUT}]; three exact "
-                  f"fp64 GEMMs of {rows}x{K_IN}x{N_OUT}); {dt:.2f} s",
+        "sample": f"one oracle fwd+bwd step on the first {rows} of {M_TOK} token rows: casts of "
+                  f"X[{rows}x{K_IN}], W[{K_IN}x{N_OUT}], dY[{rows}x{N_OUT}] (numpy, one thread) "
+                  f"and the three exact fp64 GEMMs of that sample (BLAS threads: {blas or 'n/a'}, "
+                  f"usable cores {cores}); {dt:.2f} s",
         "seconds": round(dt, 3),
     }
+
+
+def copy_calibration(torch, mib: int):
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes": n, "copies": 5}), flush=True)
+
+
+def time_launches(torch, stream, fn, iters):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def stress_cast(torch, dsg, workloads, dev, iters=10):
+    """Standalone amax+cast of 2^30 bf16 elements to E4M3 and E5M2 (3 B/element)."""
+    n = 1 << 30
+    print("[bench] stress cast 2^30", file=sys.stderr, flush=True)
+    bits = workloads.big_cast_input(n)
+    x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    del bits
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    s = torch.ones(1, dtype=torch.float32, device=dev)
+    am = torch.zeros(1, dtype=torch.float32, device=dev)
+    sat = torch.zeros(1, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for fmt, name in ((dsg.E4M3, "e4m3"), (dsg.E5M2, "e5m2")):
+        dsg.fp8ds_cast(x, fmt, s, q, None, None, am, sat)
+        ms = time_launches(torch, stream, lambda: dsg.fp8ds_cast(x, fmt, s, q, None, None, am, sat),
+                           iters)
+        gbps = 3.0 * n / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                     "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "saturated": int(sat.item())}
+    ms = time_launches(torch, stream, lambda: dsg.fp8ds_amax(x, am), iters)
+    out["amax"] = {"ms": round(ms, 4), "GB/s": round(2.0 * n / (ms * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(2.0 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    del x, q
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
-              "(the multi-GPU design is described, not built)", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU only "
+              "(how the Linear would shard over several GPUs is described, not built)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
 
+    if args.copy_calib:
+        copy_calibration(torch, args.copy_calib)
+        return
+
     import delayed_scaling_gemm_amd as dsg
     import workloads
+    from delayed_scaling_gemm_amd import (E4M3, E5M2, MMA_FP8, OP_N, OP_T, fp8ds_cast,
+                                          fp8ds_gemm, fp8ds_scale_update)
     from delayed_scaling_gemm_amd.linear import DelayedScalingLinear
 
     dev = torch.device("cuda:0")
@@ -102,21 +203,15 @@ def main():
 
     lin = DelayedScalingLinear(hist_len=HIST_LEN, algo=dsg.ALGO_MAX, margin=0, device=dev)
     stream = torch.cuda.current_stream()
+    M, K, N = M_TOK, K_IN, N_OUT
 
-    # the step, with an event after each launch so per-kernel times are measured live
-    names = ["cast_x", "cast_w", "gemm_nn_fwd", "cast_dy", "gemm_nt_dgrad", "gemm_tn_wgrad",
+    names = ["cast_x", "cast_w_t", "gemm_fwd_nt", "cast_dy", "gemm_dgrad_nt", "gemm_wgrad_tn",
              "scale_update"]
 
     def step_with_events(x, w, dy, ev):
-        from delayed_scaling_gemm_amd import (E4M3, E5M2, OP_N, OP_T, fp8ds_cast, fp8ds_gemm,
-                                              fp8ds_scale_update)
-        M, K = x.shape
-        N = w.shape[1]
-        bufs = lin._bufs
-        if "xq" not in bufs:
-            lin.step(x, w, dy)  # allocates the output buffers once
-        xq, wq, wqt, y, dyq, dx, dw = (bufs[k] for k in ("xq", "wq", "wqt", "y", "dyq", "dx",
-                                                           "dw"))
+        """The same launches as DelayedScalingLinear.step, with an event after each."""
+        b = lin._bufs
+        xq, wq, wqt, y, dyq, dx, dw = (b[k] for k in ("xq", "wq", "wqt", "y", "dyq", "dx", "dw"))
         s, su, am, sat = lin.scale, lin.scale_used, lin.amax, lin.sat
         ev[0].record(stream)
         fp8ds_cast(x, E4M3, s[0:1], xq, None, su[0:1], am[0:1], sat[0:1])
@@ -135,9 +230,9 @@ def main():
         fp8ds_scale_update(lin.history, lin.cursor, am, lin.fmts, lin.algo, lin.margin, s)
         ev[7].record(stream)
 
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, 1)):
         x, w, dy = sets[i % N_SETS]
-        lin.step(x, w, dy)
+        lin.step(x, w, dy)  # also allocates the output buffers
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
@@ -154,16 +249,18 @@ def main():
                     for i in range(args.steps)])  # ms
     step_ms = np.array([evs[i][0].elapsed_time(evs[i][7]) for i in range(args.steps)])
     ms_per_step = float(step_ms.mean())
-    flop_gemm = 2.0 * M_TOK * K_IN * N_OUT
+    flop_gemm = 2.0 * M * K * N
     value = 3 * flop_gemm / (ms_per_step * 1e-3) / 1e12
     avg = {n: float(per[:, j].mean()) for j, n in enumerate(names)}
-    gemm_tflops = {n: round(flop_gemm / (avg[n] * 1e-3) / 1e12, 1)
-                   for n in ("gemm_nn_fwd", "gemm_nt_dgrad", "gemm_tn_wgrad")}
-    cast_bytes = {"cast_x": M_TOK * K_IN * 3, "cast_w": K_IN * N_OUT * 3,
-                  "cast_dy": M_TOK * N_OUT * 3}
+    gemms = ("gemm_fwd_nt", "gemm_dgrad_nt", "gemm_wgrad_tn")
+    gemm_tflops = {n: round(flop_gemm / (avg[n] * 1e-3) / 1e12, 1) for n in gemms}
+    # algorithmic bytes of the casts: read the input (2 B), write the FP8 bytes (1 B)
+    cast_bytes = {"cast_x": M * K * 3, "cast_w_t": K * N * 3, "cast_dy": M * N * 3}
     cast_gbps = {n: round(b / (avg[n] * 1e-3) / 1e9, 1) for n, b in cast_bytes.items()}
-    dom = max(gemm_tflops, key=lambda n: avg[n])
+    dom = max(gemms, key=lambda n: avg[n])
     achieved = flop_gemm / (avg[dom] * 1e-3) / 1e12
+    traffic = measured_traffic(dom)
+
     result = {
         "metric": "FP8 scaled-GEMM TFLOP/s (% FP8 MFMA peak); amax+cast GB/s (% HBM peak)",
         "value": round(value, 1),
@@ -176,11 +273,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8",
-        "data": "synthetic",
+        "data": "synthetic (seeded; X ~ N(0,1), W ~ N(0,0.02^2), heavy-tailed dY), bf16 inputs",
         "config": {
             "workload": "fwd+bwd FP8 delayed-scaling Linear, 4096 hidden, M=16384 tokens "
-                        "(X, W, dY bf16; HYBRID E4M3/E5M2; history 16, max, margin 0)",
-            "M": M_TOK, "K": K_IN, "N": N_OUT, "hist_len": HIST_LEN,
+                        "(X, W, dY bf16; HYBRID E4M3/E5M2; history 16, max, margin 0; "
+                        "exact F16-widened GEMM datapath)",
+            "M": M, "K": K, "N": N, "hist_len": HIST_LEN,
         },
         "roofline": {
             "kernel": dom,
@@ -189,7 +287,9 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "peak_f16_mfma": PEAK_F16_TFLOPS,
+            "frac_f16_mfma": round(achieved / PEAK_F16_TFLOPS, 4),
         },
         "cast_roofline": {
             "kernel": "cast_x",
@@ -205,53 +305,35 @@ def main():
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
     }
 
+    if not args.no_fp8_path:
+        # context only: the same three GEMMs on the FP8 matrix instructions, whose
+        # summation drops small products (not the product path, see fp8ds_mma)
+        b = lin._bufs
+        su = lin.scale_used
+        calls = {
+            "gemm_fwd_nt": lambda: fp8ds_gemm(OP_N, OP_T, M, N, K, b["xq"], E4M3, K, su[0:1],
+                                              b["wqt"], E4M3, K, su[1:2], b["y"], N, None,
+                                              mma=MMA_FP8),
+            "gemm_dgrad_nt": lambda: fp8ds_gemm(OP_N, OP_T, M, K, N, b["dyq"], E5M2, N, su[2:3],
+                                                b["wq"], E4M3, N, su[1:2], b["dx"], K, None,
+                                                mma=MMA_FP8),
+            "gemm_wgrad_tn": lambda: fp8ds_gemm(OP_T, OP_N, K, N, M, b["xq"], E4M3, K, su[0:1],
+                                                b["dyq"], E5M2, N, su[2:3], b["dw"], N, None,
+                                                mma=MMA_FP8),
+        }
+        fp8 = {}
+        for n, fn in calls.items():
+            fn()
+            ms = time_launches(torch, stream, fn, 10)
+            fp8[n] = round(flop_gemm / (ms * 1e-3) / 1e12, 1)
+        result["fp8_mma_path_tflops"] = fp8
+
     if not args.no_stress:
         result["cast_stress"] = stress_cast(torch, dsg, workloads, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(xb, wb, dyb)
     print(json.dumps(result), flush=True)
-
-
-def stress_cast(torch, dsg, workloads, dev, iters=10):
-    """Standalone amax+cast of 2^30 bf16 elements to E4M3 and E5M2 (3 B/element)."""
-    n = 1 << 30
-    print("[bench] stress cast 2^30", file=sys.stderr, flush=True)
-    bits = workloads.big_cast_input(n)
-    x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    del bits
-    q = torch.empty(n, dtype=torch.uint8, device=dev)
-    s = torch.ones(1, dtype=torch.float32, device=dev)
-    am = torch.zeros(1, dtype=torch.float32, device=dev)
-    sat = torch.zeros(1, dtype=torch.int64, device=dev)
-    out = {}
-    stream = torch.cuda.current_stream()
-    for fmt, name in ((dsg.E4M3, "e4m3"), (dsg.E5M2, "e5m2")):
-        dsg.fp8ds_cast(x, fmt, s, q, None, None, am, sat)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(iters):
-            dsg.fp8ds_cast(x, fmt, s, q, None, None, am, sat)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / iters
-        gbps = 3.0 * n / (ms * 1e-3) / 1e9
-        out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
-                     "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "saturated": int(sat.item())}
-    # standalone amax (2 B/element)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(iters):
-        dsg.fp8ds_amax(x, am)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
-    out["amax"] = {"ms": round(ms, 4), "GB/s": round(2.0 * n / (ms * 1e-3) / 1e9, 1)}
-    del x, q
-    torch.cuda.empty_cache()
-    return out
 
 
 if __name__ == "__main__":
