@@ -101,3 +101,58 @@ class DelayedScalingLinear:
         fp8ds_scale_update(self.history[:n_upd], self.cursor[:n_upd], am[:n_upd],
                            self.fmts[:n_upd], self.algo, self.margin, s[:n_upd], None, stream)
         return out
+
+
+class BatchedDelayedScalingLinear:
+    """Forward pass of ``batch`` independent small Linears, each with its own
+    delayed-scaling state for X and W: three launches per step (one batched
+    cast of all X and W tensors is two calls, one batched GEMM, one scale
+    update over all 2 * batch histories) instead of several per problem.
+
+    Histories are laid out [X_0 .. X_{B-1}, W_0 .. W_{B-1}].
+    """
+
+    def __init__(self, batch: int, hist_len: int = 16, algo: int = ALGO_MAX, margin: int = 0,
+                 fmt: int = E4M3, device="cuda"):
+        self.batch = batch
+        self.hist_len = hist_len
+        self.algo = algo
+        self.margin = margin
+        self.fmt = fmt
+        self.device = torch.device(device)
+        f32 = dict(dtype=torch.float32, device=self.device)
+        n = 2 * batch
+        self.history = torch.zeros(n, hist_len, **f32)
+        self.cursor = torch.zeros(n, dtype=torch.int32, device=self.device)
+        self.scale = torch.ones(n, **f32)
+        self.scale_used = torch.zeros(n, **f32)
+        self.amax = torch.zeros(n, **f32)
+        self.sat = torch.zeros(n, dtype=torch.int64, device=self.device)
+        self.amax_y = torch.zeros(batch, **f32)
+        self._bufs = {}
+
+    def _buf(self, name, shape, dtype):
+        t = self._bufs.get(name)
+        if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+            t = torch.empty(shape, dtype=dtype, device=self.device)
+            self._bufs[name] = t
+        return t
+
+    def step(self, x, w, stream=None):
+        """x: [B, M, K], w: [B, K, N] (bf16 or fp32, contiguous) -> dict of xq, wq, y."""
+        from . import fp8ds_cast_batched, fp8ds_gemm_batched
+
+        B, M, K = x.shape
+        B2, K2, N = w.shape
+        assert B == B2 == self.batch and K == K2
+        xq = self._buf("xq", (B, M, K), torch.uint8)
+        wq = self._buf("wq", (B, K, N), torch.uint8)
+        y = self._buf("y", (B, M, N), torch.bfloat16)
+        s, su, am, sat = self.scale, self.scale_used, self.amax, self.sat
+        fp8ds_cast_batched(x, self.fmt, s[:B], xq, su[:B], am[:B], sat[:B], stream)
+        fp8ds_cast_batched(w, self.fmt, s[B:], wq, su[B:], am[B:], sat[B:], stream)
+        fp8ds_gemm_batched(OP_N, OP_N, M, N, K, B, xq, self.fmt, K, M * K, su[:B], wq, self.fmt,
+                           N, K * N, su[B:], y, N, M * N, self.amax_y, stream)
+        fp8ds_scale_update(self.history, self.cursor, am, [self.fmt] * (2 * B), self.algo,
+                           self.margin, s, None, stream)
+        return {"xq": xq, "wq": wq, "y": y}
