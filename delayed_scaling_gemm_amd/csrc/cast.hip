@@ -40,10 +40,36 @@ __global__ void prologue_kernel(int64_t count, const float* __restrict__ scale,
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
+// Four codes in one dword (first value in the low byte) with the software
+// encoder: any input, NaN included.
 template <int FMT>
-__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+__device__ __forceinline__ uint32_t encode4_sw(float a, float b, float c, float d) {
   return encode_fp8<FMT>(a) | (encode_fp8<FMT>(b) << 8) | (encode_fp8<FMT>(c) << 16) |
          (encode_fp8<FMT>(d) << 24);
+}
+
+// Four codes with gfx950's packed converts, for inputs that are not NaN.  The
+// converts round to nearest even exactly as the definition does for every value
+// within the format's range (subnormals and ties included) but turn larger
+// magnitudes into NaN (E4M3) or infinity (E5M2); clamping to +-max first gives
+// the saturating result, since max is itself a code.  Over all 2^32 fp32 inputs
+// that are not NaN this equals the software encoder bit for bit.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4_hw(float a, float b, float c, float d) {
+  constexpr float MX = FmtTraits<FMT>::kMax;
+  a = __builtin_amdgcn_fmed3f(a, -MX, MX);
+  b = __builtin_amdgcn_fmed3f(b, -MX, MX);
+  c = __builtin_amdgcn_fmed3f(c, -MX, MX);
+  d = __builtin_amdgcn_fmed3f(d, -MX, MX);
+  int w;
+  if constexpr (FMT == kE4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  }
+  return (uint32_t)w;
 }
 
 template <int FMT>
@@ -53,20 +79,26 @@ __device__ __forceinline__ uint32_t sat4(float a, float b, float c, float d) {
          (uint32_t)(fabsf(d) > M);
 }
 
-// Process 16 consecutive elements already loaded as 4 dwords of bf16 pairs (x2)
-// or 4 x 4 floats.  Returns the 16 codes; accumulates amax bits and saturations.
+// Process 16 consecutive elements already loaded as 8 dwords of bf16 pairs or 16
+// floats.  Returns the 16 codes; accumulates amax bits and saturations.  The
+// group's largest magnitude (needed for amax anyway) tells whether any element
+// is NaN; only such groups take the software encoder.
 template <int FMT>
 __device__ __forceinline__ u32x4 cast16_bf16(const uint32_t (&d)[8], float s, u16x2& amax2,
                                               uint32_t& sat, bool want_sat) {
+  u16x2 gm = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    gm = __builtin_elementwise_max(gm, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
+  amax2 = __builtin_elementwise_max(amax2, gm);
+  const bool nan = gm.x > 0x7F80u || gm.y > 0x7F80u;
   u32x4 out;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint32_t d0 = d[2 * j], d1 = d[2 * j + 1];
-    u16x2 m0 = __builtin_bit_cast(u16x2, d0 & 0x7FFF7FFFu);
-    u16x2 m1 = __builtin_bit_cast(u16x2, d1 & 0x7FFF7FFFu);
-    amax2 = __builtin_elementwise_max(amax2, __builtin_elementwise_max(m0, m1));
-    float a = bf16_lo(d0) * s, b = bf16_hi(d0) * s, c = bf16_lo(d1) * s, e = bf16_hi(d1) * s;
-    out[j] = encode4<FMT>(a, b, c, e);
+    const uint32_t d0 = d[2 * j], d1 = d[2 * j + 1];
+    const float a = bf16_lo(d0) * s, b = bf16_hi(d0) * s, c = bf16_lo(d1) * s,
+                e = bf16_hi(d1) * s;
+    out[j] = nan ? encode4_sw<FMT>(a, b, c, e) : encode4_hw<FMT>(a, b, c, e);
     if (want_sat) sat += sat4<FMT>(a, b, c, e);
   }
   return out;
@@ -75,17 +107,18 @@ __device__ __forceinline__ u32x4 cast16_bf16(const uint32_t (&d)[8], float s, u1
 template <int FMT>
 __device__ __forceinline__ u32x4 cast16_f32(const uint32_t (&d)[16], float s, uint32_t& amax,
                                              uint32_t& sat, bool want_sat) {
+  uint32_t gm = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) gm = max(gm, d[i] & 0x7FFFFFFFu);
+  amax = max(amax, gm);
+  const bool nan = gm > 0x7F800000u;
   u32x4 out;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t b = d[4 * j + i];
-      amax = max(amax, b & 0x7FFFFFFFu);
-      v[i] = __uint_as_float(b) * s;
-    }
-    out[j] = encode4<FMT>(v[0], v[1], v[2], v[3]);
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(d[4 * j + i]) * s;
+    out[j] = nan ? encode4_sw<FMT>(v[0], v[1], v[2], v[3]) : encode4_hw<FMT>(v[0], v[1], v[2], v[3]);
     if (want_sat) sat += sat4<FMT>(v[0], v[1], v[2], v[3]);
   }
   return out;
@@ -123,19 +156,27 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs p) {
     const uint16_t* x = static_cast<const uint16_t*>(p.x) + b * p.stride_x;
     uint8_t* q = WRITE_Q ? p.q + b * p.stride_q : nullptr;
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-    for (int64_t g = tid; g < ngroups; g += nthreads) {
-      u32x4 v0 = xv[2 * g];
-      u32x4 v1 = xv[2 * g + 1];
-      uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    auto one = [&](const u32x4& v0, const u32x4& v1, int64_t g) {
+      const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       if constexpr (WRITE_Q) {
-        u32x4 c = cast16_bf16<FMT>(d, s, amax2, sat, want_sat);
+        const u32x4 c = cast16_bf16<FMT>(d, s, amax2, sat, want_sat);
         reinterpret_cast<u32x4*>(q)[g] = c;
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
       }
+    };
+    // two groups per thread per iteration, both loads issued first
+    int64_t g = tid;
+    for (; g + nthreads < ngroups; g += 2 * nthreads) {
+      const int64_t g2 = g + nthreads;
+      const u32x4 a0 = xv[2 * g], a1 = xv[2 * g + 1];
+      const u32x4 b0 = xv[2 * g2], b1 = xv[2 * g2 + 1];
+      one(a0, a1, g);
+      one(b0, b1, g2);
     }
+    if (g < ngroups) one(xv[2 * g], xv[2 * g + 1], g);
     // ragged tail: fewer than 16 elements, one per thread
     const int64_t t0 = ngroups << 4;
     if (tid < n - t0) {
