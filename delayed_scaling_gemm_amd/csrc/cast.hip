@@ -139,16 +139,39 @@ struct CastArgs {
   unsigned long long* sat;  // [batch] or null
 };
 
+// Groups of 16 elements per thread per launch: each workgroup of T threads owns
+// the contiguous range of T * kGroups groups starting at blockIdx.x * T * kGroups
+// (thread t takes groups base + t + T k), issues all its loads before
+// converting, and streams with non-temporal loads and stores (the input is read
+// once; keeping it out of the caches measured faster).  A launch covers the whole
+// tensor once (no grid-stride loop), so workgroups retire in address order and
+// new ones start at once.  Atomics on one address serialise (about 11 ns each),
+// so workgroups are large (1024 threads: few resident workgroups all meeting the
+// freshly reset amax at once) and skip the amax atomic when the global value
+// already covers theirs (see block_commit_amax_sat).
+#ifndef FP8DS_CAST_GROUPS
+#define FP8DS_CAST_GROUPS 4
+#endif
+#ifndef FP8DS_CAST_THREADS
+#define FP8DS_CAST_THREADS 1024
+#endif
+template <bool BF16>
+struct CastGroups {
+  static constexpr int kGroups = FP8DS_CAST_GROUPS;    // groups per thread
+  static constexpr int kThreads = FP8DS_CAST_THREADS;  // threads per workgroup
+};
+
 template <bool BF16, int FMT, bool WRITE_Q>
-__global__ __launch_bounds__(256) void cast_kernel(CastArgs p) {
-  __shared__ uint32_t red[8];
+__global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastArgs p) {
+  constexpr int G = CastGroups<BF16>::kGroups;
+  constexpr int T = CastGroups<BF16>::kThreads;
+  __shared__ uint32_t red[2 * (T / 64)];
   const int b = blockIdx.y;
   const float s = WRITE_Q ? p.scale[b] : 1.0f;
   const bool want_sat = WRITE_Q && p.sat != nullptr;
   const int64_t n = p.n;
   const int64_t ngroups = n >> 4;
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  const int64_t base = (int64_t)blockIdx.x * T * G + threadIdx.x;
   uint32_t amax = 0, sat = 0;
   u16x2 amax2 = {0, 0};
 
@@ -156,36 +179,40 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs p) {
     const uint16_t* x = static_cast<const uint16_t*>(p.x) + b * p.stride_x;
     uint8_t* q = WRITE_Q ? p.q + b * p.stride_q : nullptr;
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-    auto one = [&](const u32x4& v0, const u32x4& v1, int64_t g) {
-      const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      if constexpr (WRITE_Q) {
-        const u32x4 c = cast16_bf16<FMT>(d, s, amax2, sat, want_sat);
-        reinterpret_cast<u32x4*>(q)[g] = c;
-      } else {
+    u32x4 v[G][2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
+    for (int k = 0; k < G; ++k) {
+      const int64_t g = base + T * k;
+      if (g < ngroups) {
+        v[k][0] = __builtin_nontemporal_load(&xv[2 * g]);
+        v[k][1] = __builtin_nontemporal_load(&xv[2 * g + 1]);
       }
-    };
-    // two groups per thread per iteration, both loads issued first
-    int64_t g = tid;
-    for (; g + nthreads < ngroups; g += 2 * nthreads) {
-      const int64_t g2 = g + nthreads;
-      const u32x4 a0 = xv[2 * g], a1 = xv[2 * g + 1];
-      const u32x4 b0 = xv[2 * g2], b1 = xv[2 * g2 + 1];
-      one(a0, a1, g);
-      one(b0, b1, g2);
     }
-    if (g < ngroups) one(xv[2 * g], xv[2 * g + 1], g);
-    // ragged tail: fewer than 16 elements, one per thread
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int64_t g = base + T * k;
+      if (g < ngroups) {
+        const uint32_t d[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w,
+                               v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
+        if constexpr (WRITE_Q) {
+          const u32x4 c = cast16_bf16<FMT>(d, s, amax2, sat, want_sat);
+          __builtin_nontemporal_store(c, reinterpret_cast<u32x4*>(q) + g);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
+        }
+      }
+    }
+    // ragged tail: fewer than 16 elements, taken by the first threads of block 0
     const int64_t t0 = ngroups << 4;
-    if (tid < n - t0) {
-      uint32_t bits = x[t0 + tid];
+    if (blockIdx.x == 0 && threadIdx.x < n - t0) {
+      const uint32_t bits = x[t0 + threadIdx.x];
       amax = max(amax, (bits & 0x7FFFu) << 16);
       if constexpr (WRITE_Q) {
-        float v = __uint_as_float(bits << 16) * s;
-        q[t0 + tid] = (uint8_t)encode_fp8<FMT>(v);
-        if (want_sat) sat += (uint32_t)(fabsf(v) > FmtTraits<FMT>::kMax);
+        const float vv = __uint_as_float(bits << 16) * s;
+        q[t0 + threadIdx.x] = (uint8_t)encode_fp8<FMT>(vv);
+        if (want_sat) sat += (uint32_t)(fabsf(vv) > FmtTraits<FMT>::kMax);
       }
     }
     amax = max(amax, ((uint32_t)max(amax2.x, amax2.y)) << 16);
@@ -193,29 +220,42 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs p) {
     const uint32_t* x = static_cast<const uint32_t*>(p.x) + b * p.stride_x;
     uint8_t* q = WRITE_Q ? p.q + b * p.stride_q : nullptr;
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-    for (int64_t g = tid; g < ngroups; g += nthreads) {
-      uint32_t d[16];
+    u32x4 v[G][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x4 v = xv[4 * g + i];
-        d[4 * i] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
+    for (int k = 0; k < G; ++k) {
+      const int64_t g = base + T * k;
+      if (g < ngroups) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[k][i] = __builtin_nontemporal_load(&xv[4 * g + i]);
       }
-      if constexpr (WRITE_Q) {
-        u32x4 c = cast16_f32<FMT>(d, s, amax, sat, want_sat);
-        reinterpret_cast<u32x4*>(q)[g] = c;
-      } else {
+    }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) amax = max(amax, d[i] & 0x7FFFFFFFu);
+    for (int k = 0; k < G; ++k) {
+      const int64_t g = base + T * k;
+      if (g < ngroups) {
+        uint32_t d[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          d[4 * i] = v[k][i].x; d[4 * i + 1] = v[k][i].y; d[4 * i + 2] = v[k][i].z;
+          d[4 * i + 3] = v[k][i].w;
+        }
+        if constexpr (WRITE_Q) {
+          const u32x4 c = cast16_f32<FMT>(d, s, amax, sat, want_sat);
+          __builtin_nontemporal_store(c, reinterpret_cast<u32x4*>(q) + g);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) amax = max(amax, d[i] & 0x7FFFFFFFu);
+        }
       }
     }
     const int64_t t0 = ngroups << 4;
-    if (tid < n - t0) {
-      uint32_t bits = x[t0 + tid];
+    if (blockIdx.x == 0 && threadIdx.x < n - t0) {
+      const uint32_t bits = x[t0 + threadIdx.x];
       amax = max(amax, bits & 0x7FFFFFFFu);
       if constexpr (WRITE_Q) {
-        float v = __uint_as_float(bits) * s;
-        q[t0 + tid] = (uint8_t)encode_fp8<FMT>(v);
-        if (want_sat) sat += (uint32_t)(fabsf(v) > FmtTraits<FMT>::kMax);
+        const float vv = __uint_as_float(bits) * s;
+        q[t0 + threadIdx.x] = (uint8_t)encode_fp8<FMT>(vv);
+        if (want_sat) sat += (uint32_t)(fabsf(vv) > FmtTraits<FMT>::kMax);
       }
     }
   }
@@ -250,6 +290,10 @@ __device__ __forceinline__ void transpose4x4_b(uint32_t i0, uint32_t i1, uint32_
   o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
+// Row tiles per workgroup (walked in sequence, one amax/saturation commit):
+// fewer workgroups meeting the freshly reset amax at once.
+constexpr int kTransposeTiles = 4;
+
 template <bool BF16, int FMT>
 __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restrict__ xp,
                                                              int64_t rows, int64_t cols,
@@ -262,92 +306,96 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restr
   __shared__ __attribute__((aligned(16))) uint8_t tile[T * T];
   __shared__ uint32_t red[8];
   const float s = scale[0];
-  const int64_t r0 = (int64_t)blockIdx.y * T;
   const int64_t c0 = (int64_t)blockIdx.x * T;
   const int tid = threadIdx.x;
   uint32_t amax = 0, sat = 0;
-  // vector path: whole tile inside, 16-element pieces aligned for 16-byte
-  // accesses in x, q and q_t
-  const bool vec = (r0 + T <= rows) && (c0 + T <= cols) && (cols % 16 == 0) && (rows % 16 == 0);
-  if (vec) {
+  for (int ti = 0; ti < kTransposeTiles; ++ti) {
+    const int64_t r0 = ((int64_t)blockIdx.y * kTransposeTiles + ti) * T;
+    if (r0 >= rows) break;
+    if (ti > 0) __syncthreads();  // the previous tile's transposed reads are done
+    // vector path: whole tile inside, 16-element pieces aligned for 16-byte
+    // accesses in x, q and q_t
+    const bool vec = (r0 + T <= rows) && (c0 + T <= cols) && (cols % 16 == 0) && (rows % 16 == 0);
+    if (vec) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int piece = tid + 256 * i;
-      const int r = piece >> 3, cp = (piece & 7) * 16;
-      const int64_t off = (r0 + r) * cols + c0 + cp;
-      u32x4 codes;
-      if constexpr (BF16) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xp) + off);
-        const u32x4 v0 = src[0], v1 = src[1];
-        const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        u16x2 amax2 = {0, 0};
-        codes = cast16_bf16<FMT>(d, s, amax2, sat, g_sat != nullptr);
-        amax = max(amax, ((uint32_t)max(amax2.x, amax2.y)) << 16);
-      } else {
-        const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(xp) + off);
-        uint32_t d[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const u32x4 v = src[k];
-          d[4 * k] = v.x; d[4 * k + 1] = v.y; d[4 * k + 2] = v.z; d[4 * k + 3] = v.w;
-        }
-        codes = cast16_f32<FMT>(d, s, amax, sat, g_sat != nullptr);
-      }
-      *reinterpret_cast<u32x4*>(q + off) = codes;
-      *reinterpret_cast<u32x4*>(tile + r * T + cp) = codes;
-    }
-    __syncthreads();
-    {
-      const int cb = tid & 31;  // 4-column block
-      const int rb = tid >> 5;  // 16-row block
-      uint32_t w[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        w[j] = *reinterpret_cast<const uint32_t*>(tile + (rb * 16 + j) * T + cb * 4);
-      uint32_t col[4][4];  // col[c][g]: rows 4g..4g+3 of column 4 cb + c
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        transpose4x4_b(w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3], col[0][g], col[1][g],
-                       col[2][g], col[3][g]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int64_t oc = c0 + cb * 4 + c;
-        *reinterpret_cast<u32x4*>(qt + oc * rows + r0 + rb * 16) =
-            u32x4{col[c][0], col[c][1], col[c][2], col[c][3]};
-      }
-    }
-  } else {
-    const int tr = tid >> 1;         // row within the tile
-    const int tc = (tid & 1) * 64;   // first of this thread's 64 columns
-    const int64_t r = r0 + tr;
-    for (int i = 0; i < 64; ++i) {
-      const int64_t c = c0 + tc + i;
-      uint32_t code = 0;
-      if (r < rows && c < cols) {
-        float v;
+      for (int i = 0; i < 4; ++i) {
+        const int piece = tid + 256 * i;
+        const int r = piece >> 3, cp = (piece & 7) * 16;
+        const int64_t off = (r0 + r) * cols + c0 + cp;
+        u32x4 codes;
         if constexpr (BF16) {
-          const uint32_t bits = static_cast<const uint16_t*>(xp)[r * cols + c];
-          amax = max(amax, (bits & 0x7FFFu) << 16);
-          v = __uint_as_float(bits << 16) * s;
+          const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xp) + off);
+          const u32x4 v0 = src[0], v1 = src[1];
+          const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          u16x2 amax2 = {0, 0};
+          codes = cast16_bf16<FMT>(d, s, amax2, sat, g_sat != nullptr);
+          amax = max(amax, ((uint32_t)max(amax2.x, amax2.y)) << 16);
         } else {
-          const uint32_t bits = static_cast<const uint32_t*>(xp)[r * cols + c];
-          amax = max(amax, bits & 0x7FFFFFFFu);
-          v = __uint_as_float(bits) * s;
+          const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(xp) + off);
+          uint32_t d[16];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const u32x4 v = src[k];
+            d[4 * k] = v.x; d[4 * k + 1] = v.y; d[4 * k + 2] = v.z; d[4 * k + 3] = v.w;
+          }
+          codes = cast16_f32<FMT>(d, s, amax, sat, g_sat != nullptr);
         }
-        code = encode_fp8<FMT>(v);
-        if (g_sat) sat += (uint32_t)(fabsf(v) > FmtTraits<FMT>::kMax);
-        q[r * cols + c] = (uint8_t)code;
+        *reinterpret_cast<u32x4*>(q + off) = codes;
+        *reinterpret_cast<u32x4*>(tile + r * T + cp) = codes;
       }
-      tile[tr * T + tc + i] = (uint8_t)code;
-    }
-    __syncthreads();
-    const int oc_l = tid >> 1;       // column within the tile
-    const int orr = (tid & 1) * 64;  // first of this thread's 64 rows
-    const int64_t oc = c0 + oc_l;
-    if (oc < cols) {
+      __syncthreads();
+      {
+        const int cb = tid & 31;  // 4-column block
+        const int rb = tid >> 5;  // 16-row block
+        uint32_t w[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          w[j] = *reinterpret_cast<const uint32_t*>(tile + (rb * 16 + j) * T + cb * 4);
+        uint32_t col[4][4];  // col[c][g]: rows 4g..4g+3 of column 4 cb + c
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          transpose4x4_b(w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3], col[0][g], col[1][g],
+                         col[2][g], col[3][g]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t oc = c0 + cb * 4 + c;
+          *reinterpret_cast<u32x4*>(qt + oc * rows + r0 + rb * 16) =
+              u32x4{col[c][0], col[c][1], col[c][2], col[c][3]};
+        }
+      }
+    } else {
+      const int tr = tid >> 1;         // row within the tile
+      const int tc = (tid & 1) * 64;   // first of this thread's 64 columns
+      const int64_t r = r0 + tr;
       for (int i = 0; i < 64; ++i) {
-        const int64_t orow = r0 + orr + i;
-        if (orow < rows) qt[oc * rows + orow] = tile[(orr + i) * T + oc_l];
+        const int64_t c = c0 + tc + i;
+        uint32_t code = 0;
+        if (r < rows && c < cols) {
+          float v;
+          if constexpr (BF16) {
+            const uint32_t bits = static_cast<const uint16_t*>(xp)[r * cols + c];
+            amax = max(amax, (bits & 0x7FFFu) << 16);
+            v = __uint_as_float(bits << 16) * s;
+          } else {
+            const uint32_t bits = static_cast<const uint32_t*>(xp)[r * cols + c];
+            amax = max(amax, bits & 0x7FFFFFFFu);
+            v = __uint_as_float(bits) * s;
+          }
+          code = encode_fp8<FMT>(v);
+          if (g_sat) sat += (uint32_t)(fabsf(v) > FmtTraits<FMT>::kMax);
+          q[r * cols + c] = (uint8_t)code;
+        }
+        tile[tr * T + tc + i] = (uint8_t)code;
+      }
+      __syncthreads();
+      const int oc_l = tid >> 1;       // column within the tile
+      const int orr = (tid & 1) * 64;  // first of this thread's 64 rows
+      const int64_t oc = c0 + oc_l;
+      if (oc < cols) {
+        for (int i = 0; i < 64; ++i) {
+          const int64_t orow = r0 + orr + i;
+          if (orow < rows) qt[oc * rows + orow] = tile[(orr + i) * T + oc_l];
+        }
       }
     }
   }
@@ -355,14 +403,6 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restr
 }
 
 // ------------------------------------------------------------------ host launchers
-
-static int grid_for(int64_t groups, int num_cus) {
-  int64_t want = (groups + 255) / 256;
-  int64_t cap = (int64_t)num_cus * 8;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  return (int)want;
-}
 
 hipError_t launch_prologue(int64_t count, const float* scale, float* scale_used, float* amax,
                            uint64_t* sat, hipStream_t stream) {
@@ -375,17 +415,14 @@ hipError_t launch_prologue(int64_t count, const float* scale, float* scale_used,
 
 template <bool BF16, int FMT, bool WRITE_Q>
 static hipError_t launch_cast_t(const CastArgs& a, int64_t batch, int num_cus, hipStream_t stream) {
-  int64_t groups = (a.n >> 4) + 1;
-  int gx = grid_for(groups, num_cus);
-  if (batch > 1) {
-    // spread ~8 blocks per CU over all tensors
-    int64_t per = ((int64_t)num_cus * 8 + batch - 1) / batch;
-    if (per < 1) per = 1;
-    int64_t want = (groups + 255) / 256;
-    gx = (int)(want < per ? (want < 1 ? 1 : want) : per);
-  }
-  hipLaunchKernelGGL((cast_kernel<BF16, FMT, WRITE_Q>), dim3(gx, (unsigned)batch), dim3(256), 0,
-                     stream, a);
+  (void)num_cus;
+  constexpr int64_t T = CastGroups<BF16>::kThreads;
+  constexpr int64_t per_block = T * CastGroups<BF16>::kGroups;
+  const int64_t groups = a.n >> 4;
+  int64_t gx = (groups + per_block - 1) / per_block;
+  if (gx < 1) gx = 1;  // block 0 also takes the ragged tail (fewer than 16 elements)
+  hipLaunchKernelGGL((cast_kernel<BF16, FMT, WRITE_Q>), dim3((unsigned)gx, (unsigned)batch),
+                     dim3((unsigned)T), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -409,7 +446,8 @@ hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64
 hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
                                  const float* scale, uint8_t* q, uint8_t* qt, float* amax,
                                  uint64_t* sat, hipStream_t stream) {
-  dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+  dim3 grid((unsigned)((cols + 127) / 128),
+            (unsigned)(((rows + 127) / 128 + kTransposeTiles - 1) / kTransposeTiles));
   uint32_t* am = reinterpret_cast<uint32_t*>(amax);
   unsigned long long* st = reinterpret_cast<unsigned long long*>(sat);
   if (bf16) {

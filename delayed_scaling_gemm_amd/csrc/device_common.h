@@ -92,7 +92,7 @@ __device__ __forceinline__ void block_commit_amax_sat(uint32_t amax_bits, uint32
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
   if (g_amax) amax_bits = wave_max_u32(amax_bits);
-  if (g_sat) sat = wave_sum_u32(sat);
+  if (g_sat && __any(sat != 0)) sat = wave_sum_u32(sat);  // most waves saturate nothing
   if (lane == 0) {
     smem[wave] = amax_bits;
     smem[nwaves + wave] = sat;
@@ -104,7 +104,13 @@ __device__ __forceinline__ void block_commit_amax_sat(uint32_t amax_bits, uint32
       m = max(m, smem[w]);
       s += smem[nwaves + w];
     }
-    if (g_amax) atomicMax(g_amax, canonical_amax_bits(m));
+    if (g_amax) {
+      // The global value only grows, so a workgroup whose maximum is already
+      // covered can skip the atomic (a stale read only costs an extra atomic).
+      const uint32_t mb = canonical_amax_bits(m);
+      if (mb > __hip_atomic_load(g_amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        atomicMax(g_amax, mb);
+    }
     if (g_sat && s) atomicAdd(g_sat, (unsigned long long)s);
   }
 }
