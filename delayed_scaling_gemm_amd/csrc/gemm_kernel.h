@@ -278,6 +278,46 @@ struct LoaderSel<false, ROWS, NT, KB, WIDEN, FMT> {
   using type = LoaderMN<ROWS, NT, KB, WIDEN, FMT>;
 };
 
+// KC source loaded straight into LDS (gfx950 global_load_lds_dwordx4: each
+// lane's 16 bytes land at LDS base + 16 * lane, no registers involved).  A
+// wave instruction fills one 1 KiB segment = 8 LDS rows of 128 bytes; lane l
+// takes physical chunk l % 8 of row l / 8 and therefore loads the logical chunk
+// (l % 8) ^ swz(row), which keeps the swizzled layout of lds_off.  Requires the
+// stage to lie inside K (K a multiple of 128); rows past the matrix are clamped
+// to its last row (they only feed outputs that are never stored).
+// Wait until every vector-memory operation of this wave has completed.  Direct
+// LDS loads write no registers, so the compiler does not wait for them on its
+// own, and a workgroup barrier's fence only waits for LDS operations.
+// (s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt unconstrained.)
+__device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int ROWS, int NT>
+struct LoaderKCDirect {
+  static constexpr int kSegs = ROWS / 8;
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kPerWave = kSegs / kWaves;
+  static_assert(kPerWave * kWaves == kSegs, "segments must divide among the waves");
+
+  __device__ __forceinline__ static void issue(const uint8_t* __restrict__ src, int64_t ld,
+                                               int64_t row0, int64_t rows, int64_t k0,
+                                               uint8_t* lds, int tid) {
+    const int lane = tid & 63, w = tid >> 6;
+    const int rr = lane >> 3, pc = lane & 7;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int seg = w * kPerWave + i;
+      const int r = seg * 8 + rr;
+      const int c = pc ^ swz(r);
+      int64_t gr = row0 + r;
+      gr = gr < rows ? gr : rows - 1;
+      const uint8_t* g = src + gr * ld + k0 + c * 16;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                       (void __attribute__((address_space(3)))*)(lds + seg * 1024),
+                                       16, 0, 0);
+    }
+  }
+};
+
 // ------------------------------------------------------------------ tile order
 
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -400,8 +440,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
 //     under step 7.
 // FP8: a stage is 2 MFMA steps of K = 64 (32x32x64 F8F6F4), each on two chunks.
 
-template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT>
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
+  static_assert(!DIRECT || (A_KC && B_KC), "direct LDS loads need K-contiguous operands");
   constexpr int NT = 256;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -482,11 +523,27 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       }
     };
 
+    // DIRECT: stages are loaded straight into LDS two stages ahead: stage k + 2
+    // goes into the buffer of stage k right after stage k's barrier (all waves
+    // have read it by then), and that barrier's wait on outstanding loads makes
+    // stage k + 1 complete before it is read.
+    auto issue_direct = [&](int kt, int buf) {
+      if constexpr (DIRECT) {
+        LoaderKCDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
+        LoaderKCDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
+      }
+    };
     if (nk > 0) {
-      la.load(A, p.lda, m0, M, 0, K, tid);
-      lb.load(B, p.ldb, n0, N, 0, K, tid);
-      la.store(lds_a[0], tid);
-      lb.store(lds_b[0], tid);
+      if constexpr (DIRECT) {
+        issue_direct(0, 0);
+        if (nk > 1) issue_direct(1, 1);
+        vmem_wait_all();
+      } else {
+        la.load(A, p.lda, m0, M, 0, K, tid);
+        lb.load(B, p.ldb, n0, N, 0, K, tid);
+        la.store(lds_a[0], tid);
+        lb.store(lds_b[0], tid);
+      }
       __syncthreads();
       read_unit(0, 0, ra[0], rb[0]);
       widen_step(ra[0], rb[0], 0, ha[0], hb[0]);
@@ -495,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     auto stage = [&](int kt, auto more_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
       const int cur = kt & 1;
-      if constexpr (MORE) {
+      if constexpr (MORE && !DIRECT) {
         la.load(A, p.lda, m0, M, (int64_t)(kt + 1) * KB, K, tid);
         lb.load(B, p.ldb, n0, N, (int64_t)(kt + 1) * KB, K, tid);
       }
@@ -504,13 +561,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         const int u = t >> 1;
         if ((t & 1) == 0 && u + 1 < 4) read_unit(cur, u + 1, ra[(u + 1) & 1], rb[(u + 1) & 1]);
         if constexpr (MORE) {
-          if (t == 4) {
-            la.store(lds_a[cur ^ 1], tid);
-            lb.store(lds_b[cur ^ 1], tid);
+          if constexpr (!DIRECT) {
+            if (t == 4) {
+              la.store(lds_a[cur ^ 1], tid);
+              lb.store(lds_b[cur ^ 1], tid);
+            }
           }
           if (t == 6) {
+            if constexpr (DIRECT) vmem_wait_all();
             __syncthreads();
             read_unit(cur ^ 1, 0, ra[0], rb[0]);
+            if constexpr (DIRECT) {
+              if (kt + 2 < nk) issue_direct(kt + 2, cur);
+            }
           }
         }
         // widen the operands of step t + 1 (the next stage's step 0 after t = 7)
@@ -595,7 +658,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 
 // ------------------------------------------------------------------ dispatch
 
-template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT>
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT>
 static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   GemmArgs a;
   a.M = q.M; a.N = q.N; a.K = q.K;
@@ -607,17 +670,27 @@ static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   a.tiles_n = (int)((q.N + BN - 1) / BN);
   a.out_f32 = q.out_bf16 ? 0 : 1;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)q.batch);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, EXACT>), grid, dim3(256), 0, stream,
-                     a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, EXACT, DIRECT>), grid, dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
+}
+
+// Both operands K-contiguous and K a multiple of the stage depth: LDS is filled
+// by direct loads (EXACT datapath); otherwise through registers.
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT>
+static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream) {
+  if constexpr (EXACT && A_KC && B_KC) {
+    if (q.K % 128 == 0) return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, true>(q, stream);
+  }
+  return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, false>(q, stream);
 }
 
 template <int BM, int BN, bool A_KC, bool B_KC, bool EXACT>
 static hipError_t launch_layout(const GemmProblem& q, hipStream_t s) {
-  if (q.fa == kE4M3 && q.fb == kE4M3) return launch_cfg<BM, BN, A_KC, B_KC, kE4M3, kE4M3, EXACT>(q, s);
-  if (q.fa == kE4M3 && q.fb == kE5M2) return launch_cfg<BM, BN, A_KC, B_KC, kE4M3, kE5M2, EXACT>(q, s);
-  if (q.fa == kE5M2 && q.fb == kE4M3) return launch_cfg<BM, BN, A_KC, B_KC, kE5M2, kE4M3, EXACT>(q, s);
-  if (q.fa == kE5M2 && q.fb == kE5M2) return launch_cfg<BM, BN, A_KC, B_KC, kE5M2, kE5M2, EXACT>(q, s);
+  if (q.fa == kE4M3 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE4M3, EXACT>(q, s);
+  if (q.fa == kE4M3 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE5M2, EXACT>(q, s);
+  if (q.fa == kE5M2 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE4M3, EXACT>(q, s);
+  if (q.fa == kE5M2 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE5M2, EXACT>(q, s);
   return hipErrorInvalidValue;
 }
 
