@@ -318,6 +318,66 @@ struct LoaderKCDirect {
   }
 };
 
+// MN source (element (k, r) at src[k * ld + r]) loaded straight into LDS in its
+// own orientation: LDS row k holds the tile's ROWS bytes of that k, split into
+// 16-byte chunks XOR-swizzled by (k % 8) (times 2 for 256-byte rows, so that the
+// 16 pieces of a 32-lane transposing read, two chunks over eight k rows, fall in
+// 16 distinct chunk columns).  A wave instruction fills 1 KiB = 1024 / ROWS
+// rows; lane l takes physical chunk l % (ROWS / 16) of its row and loads the
+// logical chunk that lands there.  Requires whole 16-byte chunks (rows a
+// multiple of 16; chunks past the matrix are clamped to its last chunk, feeding
+// only outputs that are never stored) and the stage inside K.
+template <int ROWS>
+__device__ __forceinline__ int mn_swz(int k) {
+  return ROWS >= 256 ? (k & 7) << 1 : (k & 7);
+}
+template <int ROWS>
+__device__ __forceinline__ int mn_off(int k, int r) {
+  return k * ROWS + (((r >> 4) ^ mn_swz<ROWS>(k)) << 4) + (r & 15);
+}
+
+template <int ROWS, int NT>
+struct LoaderMNDirect {
+  static constexpr int kCpr = ROWS / 16;      // chunks per LDS row
+  static constexpr int kRps = 64 / kCpr;      // LDS rows per wave instruction
+  static constexpr int kSegs = 128 / kRps;    // wave instructions per stage (128 k rows)
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kPerWave = kSegs / kWaves;
+  static_assert(kCpr >= 8 && kPerWave * kWaves == kSegs, "tile shape not supported");
+
+  __device__ __forceinline__ static void issue(const uint8_t* __restrict__ src, int64_t ld,
+                                               int64_t row0, int64_t rows, int64_t k0,
+                                               uint8_t* lds, int tid) {
+    const int lane = tid & 63, w = tid >> 6;
+    const int rr = lane / kCpr, pc = lane % kCpr;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int seg = w * kPerWave + i;
+      const int k = seg * kRps + rr;
+      const int c = pc ^ mn_swz<ROWS>(k);
+      int64_t gm = row0 + c * 16;
+      gm = gm + 16 <= rows ? gm : rows - 16;
+      const uint8_t* g = src + (k0 + k) * ld + gm;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                       (void __attribute__((address_space(3)))*)(lds + seg * 1024),
+                                       16, 0, 0);
+    }
+  }
+};
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b8).  Within each group of 16
+// lanes, lane i receives byte (i % 8) of the 8-byte pieces addressed by lanes
+// 2j + i / 8 (j = 0..7), in order.  With even lanes addressing rows
+// [r0, r0 + 8) and odd lanes rows [r0 + 8, r0 + 16) of the k rows kb + j, lane i
+// obtains row r0 + i % 8 + 8 (i / 8) at k = kb .. kb + 7: a K-contiguous MFMA
+// operand read from an MN-major tile.
+__device__ __forceinline__ u32x2 ds_read_tr8(const uint8_t* p) {
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  const v2i_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) v2i_t*)(p));
+  return u32x2{(uint32_t)v[0], (uint32_t)v[1]};
+}
+
 // ------------------------------------------------------------------ tile order
 
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -442,7 +502,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
 
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
-  static_assert(!DIRECT || (A_KC && B_KC), "direct LDS loads need K-contiguous operands");
+  static_assert(!DIRECT || EXACT, "direct LDS loads are used by the exact datapath only");
   constexpr int NT = 256;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -479,14 +539,36 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   const int fr = lane & 31;
   const int fc = (lane >> 5) * 4;  // first of this lane's four chunks
 
-  // raw chunk reads of one unit (one chunk per 32-row block)
+  // Raw operand bytes of one unit (16 K values per lane per 32-row block: the
+  // two MFMA steps 2u and 2u + 1).  K-major LDS tiles give them as one 16-byte
+  // chunk; MN-major tiles (direct loads of MN-contiguous operands) as two
+  // transposing reads of 8 bytes whose K values follow the same order.
+  constexpr bool A_MN_LDS = DIRECT && !A_KC;
+  constexpr bool B_MN_LDS = DIRECT && !B_KC;
+  const int tr_i = lane & 15;
+  const int tr_row = 16 * ((lane >> 4) & 1) + 8 * (tr_i & 1);  // row offset in a 32-row block
+  const int tr_k = 64 * (lane >> 5) + (tr_i >> 1);              // + 16 u + 8 h
+  auto read_mn = [&](const uint8_t* tile, auto rows_tag, int r0, int u) {
+    constexpr int R = decltype(rows_tag)::value;
+    const u32x2 lo = ds_read_tr8(tile + mn_off<R>(tr_k + 16 * u, r0 + tr_row));
+    const u32x2 hi = ds_read_tr8(tile + mn_off<R>(tr_k + 16 * u + 8, r0 + tr_row));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
   auto read_unit = [&](int buf, int u, u32x4 (&xa)[FM], u32x4 (&xb)[FN]) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      xb[j] = *reinterpret_cast<const u32x4*>(lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, fc + u));
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (B_MN_LDS)
+        xb[j] = read_mn(lds_b[buf], std::integral_constant<int, BN>{}, wn * WTN + j * 32, u);
+      else
+        xb[j] = *reinterpret_cast<const u32x4*>(lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, fc + u));
+    }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      xa[i] = *reinterpret_cast<const u32x4*>(lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, fc + u));
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (A_MN_LDS)
+        xa[i] = read_mn(lds_a[buf], std::integral_constant<int, BM>{}, wm * WTM + i * 32, u);
+      else
+        xa[i] = *reinterpret_cast<const u32x4*>(lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, fc + u));
+    }
   };
 
   if constexpr (EXACT) {
@@ -529,8 +611,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     // stage k + 1 complete before it is read.
     auto issue_direct = [&](int kt, int buf) {
       if constexpr (DIRECT) {
-        LoaderKCDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
-        LoaderKCDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
+        if constexpr (A_KC)
+          LoaderKCDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
+        else
+          LoaderMNDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
+        if constexpr (B_KC)
+          LoaderKCDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
+        else
+          LoaderMNDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
       }
     };
     if (nk > 0) {
@@ -675,12 +763,21 @@ static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Both operands K-contiguous and K a multiple of the stage depth: LDS is filled
-// by direct loads (EXACT datapath); otherwise through registers.
+// K a multiple of the stage depth and operands in aligned 16-byte chunks: LDS is
+// filled by direct loads (EXACT datapath); otherwise through registers.
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT>
 static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream) {
-  if constexpr (EXACT && A_KC && B_KC) {
-    if (q.K % 128 == 0) return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, true>(q, stream);
+  if constexpr (EXACT) {
+    // Direct loads move aligned 16-byte chunks; MN-contiguous operands are
+    // loaded in whole chunks along M / N.
+    auto aligned = [&](const uint8_t* ptr, int64_t ld, int64_t stride) {
+      return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && ld % 16 == 0 &&
+             (q.batch == 1 || stride % 16 == 0);
+    };
+    const bool a_ok = aligned(q.A, q.lda, q.stride_a) && (A_KC || q.M % 16 == 0);
+    const bool b_ok = aligned(q.B, q.ldb, q.stride_b) && (B_KC || q.N % 16 == 0);
+    if (q.K % 128 == 0 && a_ok && b_ok)
+      return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, true>(q, stream);
   }
   return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, false>(q, stream);
 }

@@ -123,7 +123,8 @@ def test_code_pair_table(fa, fb, mma):
 @pytest.mark.parametrize("opa,opb", LAYOUTS)
 @pytest.mark.parametrize("fa,fb", [(dsg.E4M3, dsg.E4M3), (dsg.E5M2, dsg.E4M3),
                                    (dsg.E4M3, dsg.E5M2)])
-@pytest.mark.parametrize("shape", [(300, 520, 384), (257, 129, 1000), (520, 300, 2048)])
+@pytest.mark.parametrize("shape", [(300, 520, 384), (257, 129, 1000), (520, 300, 2048),
+                                   (336, 528, 640)])
 def test_random_codes_within_tolerance(opa, opb, fa, fb, shape, mma):
     M, N, K = shape
     rng = np.random.default_rng(M + N + K + opa * 11 + opb * 13 + fa * 17 + fb * 19)
@@ -168,9 +169,10 @@ def test_zero_k_and_empty():
 
 
 @pytest.mark.parametrize("mma", MMAS)
-def test_batched_matches_oracle(mma):
-    rng = np.random.default_rng(21)
-    Bn, M, N, K = 5, 96, 80, 160
+@pytest.mark.parametrize("K", [160, 256])
+def test_batched_matches_oracle(mma, K):
+    rng = np.random.default_rng(21 + K)
+    Bn, M, N = 5, 96, 80
     ca = np.stack([finite_codes(rng, (M, K), dsg.E4M3) for _ in range(Bn)])
     cb = np.stack([finite_codes(rng, (K, N), dsg.E4M3) for _ in range(Bn)])
     sa = rng.uniform(0.5, 50, Bn).astype(np.float32)
@@ -230,3 +232,21 @@ def test_fp8_datapath_summation_window():
     C8, _ = run_gemm(dsg.OP_N, dsg.OP_N, a, dsg.E4M3, b, dsg.E4M3, 16, 16, K, mma=dsg.MMA_FP8)
     got = C8.cpu().numpy().astype(np.float64)
     assert np.all(got < exact) and np.all(got >= 1.0)
+
+
+@pytest.mark.parametrize("opa,opb", LAYOUTS)
+def test_ragged_large_tiles_exact(opa, opb):
+    """Enough tiles for the 256 x 256 configuration, with M and N one 16-wide
+    chunk past a tile edge and several K stages: small integers, compared bit
+    for bit with an exact float64 product."""
+    M, N, K = 4112, 4112, 384
+    rng = np.random.default_rng(4112 + 3 * opa + opb)
+    ca, ia = int_codes(rng, (M, K), dsg.E4M3)
+    cb, ib = int_codes(rng, (K, N), dsg.E5M2)
+    a_st = ca if opa == dsg.OP_N else np.ascontiguousarray(ca.T)
+    b_st = cb if opb == dsg.OP_N else np.ascontiguousarray(cb.T)
+    C, am = run_gemm(opa, opb, a_st, dsg.E4M3, b_st, dsg.E5M2, M, N, K)
+    exp = (ia.astype(np.float64) @ ib.astype(np.float64)).astype(np.float32)
+    got = C.cpu().numpy()
+    assert np.array_equal(got, exp), f"{np.count_nonzero(got != exp)} differ"
+    assert am == f32_bits(np.max(np.abs(exp)))
