@@ -401,73 +401,110 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 
 // ------------------------------------------------------------------ epilogue
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return ((b >> 16) & 0x8000u) | 0x7FC0u;
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+// Two FP32 values to packed BF16, round to nearest even (gfx950 v_cvt_pk_bf16_f32;
+// equal to the rounding of the definition for every non-NaN input, subnormals
+// included; a NaN stays a quiet NaN of its sign).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ u16x2_t abs_bf16x2(uint32_t v) {
+  return __builtin_bit_cast(u16x2_t, v & 0x7FFF7FFFu);
 }
 
 // Dequant, convert, store and reduce the output amax.  Lane l holds, for each
 // 32 x 32 block (i, j), row (l % 32) and the columns 8g + 4 (l / 32) + {0..3}
-// for g = 0..3 (accumulator elements 4g .. 4g+3).
-template <int FM, int FN, int WTM, int WTN>
+// for g = 0..3 (accumulator elements 4g .. 4g+3).  Tiles inside the matrix take
+// a branch-free path (row pointers per block row, immediate column offsets);
+// edge tiles check every row and group of four columns.
+template <int BM, int BN, int FM, int FN, int WTM, int WTN>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM][FN], int64_t m0,
-                                         int64_t n0, int wm, int wn, int tid, int64_t bz,
+                                         int64_t n0, int wm, int wn, int tid, int64_t bz, float d,
                                          uint32_t* red) {
   const int lane = tid & 63, wave = tid >> 6;
-  const int fr = lane & 31;
   const int64_t M = p.M, N = p.N;
-  const float d = __fdiv_rn(1.0f, p.scale_a[bz] * p.scale_b[bz]);
+  const int64_t mb = m0 + wm * WTM + (lane & 31);
+  const int64_t nb = n0 + wn * WTN + (lane >> 5) * 4;
+  const bool full = m0 + BM <= M && n0 + BN <= N;
   uint32_t amax = 0;
-  const int cq = (lane >> 5) * 4;
-  const bool f32out = p.out_f32 != 0;
+  if (!p.out_f32) {
+    uint16_t* C = static_cast<uint16_t*>(p.C) + bz * p.stride_c;
+    if (full) {
+      u16x2_t am2 = {0, 0};
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t m = m0 + wm * WTM + i * 32 + fr;
-    if (m >= M) continue;
+      for (int i = 0; i < FM; ++i) {
+        uint16_t* row = C + (mb + i * 32) * p.ldc + nb;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + cq;
-        if (n >= N) continue;
-        const float y0 = acc[i][j][4 * g] * d, y1 = acc[i][j][4 * g + 1] * d;
-        const float y2 = acc[i][j][4 * g + 2] * d, y3 = acc[i][j][4 * g + 3] * d;
-        if (!f32out) {
-          uint16_t* C = static_cast<uint16_t*>(p.C) + bz * p.stride_c + m * p.ldc + n;
-          const uint32_t h0 = f32_to_bf16_rne(y0), h1 = f32_to_bf16_rne(y1);
-          const uint32_t h2 = f32_to_bf16_rne(y2), h3 = f32_to_bf16_rne(y3);
-          if (n + 3 < N) {
-            *reinterpret_cast<u32x2*>(C) = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
-            amax = max(amax, max(max(h0 & 0x7FFFu, h1 & 0x7FFFu), max(h2 & 0x7FFFu, h3 & 0x7FFFu))
-                                 << 16);
-          } else {
-            const uint32_t hv[4] = {h0, h1, h2, h3};
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (n + v < N) {
-                C[v] = (uint16_t)hv[v];
-                amax = max(amax, (hv[v] & 0x7FFFu) << 16);
-              }
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t lo = pack_bf16x2(acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d);
+            const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d);
+            *reinterpret_cast<u32x2*>(row + j * 32 + 8 * g) = u32x2{lo, hi};
+            am2 = __builtin_elementwise_max(am2, __builtin_elementwise_max(abs_bf16x2(lo), abs_bf16x2(hi)));
           }
-        } else {
-          float* C = static_cast<float*>(p.C) + bz * p.stride_c + m * p.ldc + n;
-          const float yv[4] = {y0, y1, y2, y3};
-          if (n + 3 < N) {
-            *reinterpret_cast<u32x4*>(C) = u32x4{__float_as_uint(y0), __float_as_uint(y1),
-                                                 __float_as_uint(y2), __float_as_uint(y3)};
+      }
+      amax = (uint32_t)max(am2[0], am2[1]) << 16;
+    } else {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) amax = max(amax, __float_as_uint(yv[v]) & 0x7FFFFFFFu);
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = mb + i * 32;
+        if (m >= M) continue;
+        uint16_t* row = C + m * p.ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int64_t n = nb + j * 32 + 8 * g;
+            if (n >= N) continue;
+            const uint32_t lo = pack_bf16x2(acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d);
+            const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d);
+            const int64_t left = N - n;  // >= 1
+            const uint32_t mlo = left >= 2 ? 0x7FFF7FFFu : 0x7FFFu;
+            const uint32_t mhi = left >= 4 ? 0x7FFF7FFFu : left == 3 ? 0x7FFFu : 0u;
+            const u16x2_t m2 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, lo & mlo),
+                                                         __builtin_bit_cast(u16x2_t, hi & mhi));
+            amax = max(amax, (uint32_t)max(m2[0], m2[1]) << 16);
+            if (left >= 4) {
+              *reinterpret_cast<u32x2*>(row + n) = u32x2{lo, hi};
+            } else {
+              row[n] = (uint16_t)lo;
+              if (left >= 2) row[n + 1] = (uint16_t)(lo >> 16);
+              if (left >= 3) row[n + 2] = (uint16_t)hi;
+            }
+          }
+      }
+    }
+  } else {
+    float* C = static_cast<float*>(p.C) + bz * p.stride_c;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = mb + i * 32;
+      if (!full && m >= M) continue;
+      float* row = C + m * p.ldc;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = nb + j * 32 + 8 * g;
+          if (!full && n >= N) continue;
+          float y[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            y[v] = acc[i][j][4 * g + v] * d;
+            if (full || n + v < N) amax = max(amax, __float_as_uint(y[v]) & 0x7FFFFFFFu);
+          }
+          if (full || n + 3 < N) {
+            *reinterpret_cast<u32x4*>(row + n) = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]),
+                                                       __float_as_uint(y[2]), __float_as_uint(y[3])};
           } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (n + v < N) {
-                C[v] = yv[v];
-                amax = max(amax, __float_as_uint(yv[v]) & 0x7FFFFFFFu);
-              }
+            row[n] = y[0];
+            if (n + 1 < N) row[n + 1] = y[1];
+            if (n + 2 < N) row[n + 2] = y[2];
           }
         }
-      }
     }
   }
   if (p.amax_c) {
@@ -536,6 +573,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int nk = (int)((K + KB - 1) / KB);
+  const float d = __fdiv_rn(1.0f, p.scale_a[bz] * p.scale_b[bz]);  // dequant factor
   const int fr = lane & 31;
   const int fc = (lane >> 5) * 4;  // first of this lane's four chunks
 
@@ -741,7 +779,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     if (nk > 0) stage(nk - 1, std::false_type{});
   }
 
-  epilogue<FM, FN, WTM, WTN>(p, acc, m0, n0, wm, wn, tid, bz, red);
+  epilogue<BM, BN, FM, FN, WTM, WTN>(p, acc, m0, n0, wm, wn, tid, bz, d, red);
 }
 
 // ------------------------------------------------------------------ dispatch
