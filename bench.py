@@ -14,6 +14,12 @@ in HBM before timing; four input sets are rotated so that the 256 MB Infinity
 Cache cannot hold a step's working set.  Per-kernel times come from HIP events
 recorded between the launches on the stream the library launches on.
 
+The line also carries context figures that are not `value`: the same GEMMs on
+the FP8 matrix instructions (`fp8_mma_path_tflops`), the 2^30-element stress
+casts (`cast_stress`), and `configs`, the throughput of the other workloads
+(forward-only 4096 Linear at M = 8192, the decoder-layer projections at
+M = 8192, 512 small Linears).
+
 Prints one JSON line.  `--gpus N` with N > 1 is refused: this build measures
 one GPU.  `--copy-calib` only runs device copies of known size (the reference
 for the HBM byte counters, see profiles/).
@@ -52,6 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stress", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration throughput report")
     ap.add_argument("--no-fp8-path", action="store_true",
                     help="skip the context timing of the FP8-MFMA datapath")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -165,6 +173,88 @@ def stress_cast(torch, dsg, workloads, dev, iters=10):
     out["amax"] = {"ms": round(ms, 4), "GB/s": round(2.0 * n / (ms * 1e-3) / 1e9, 1),
                    "frac_hbm": round(2.0 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     del x, q
+    torch.cuda.empty_cache()
+    return out
+
+
+def configs_report(torch, dsg, workloads, dev, iters=5):
+    """Throughput of the other workloads, one Linear at a time: the forward-only
+    4096 Linear (M=8192, history 1024), the decoder-layer projections (M=8192,
+    fwd+bwd; v and o share the k and q shapes, up shares gate's) and the batch of
+    512 small Linears.  Step times include every launch of the step (casts, GEMMs,
+    scale update); per-GEMM rates time each GEMM call alone on the step's operands."""
+    from delayed_scaling_gemm_amd import E4M3, E5M2, OP_N, OP_T, fp8ds_gemm
+    from delayed_scaling_gemm_amd.linear import BatchedDelayedScalingLinear, DelayedScalingLinear
+
+    stream = torch.cuda.current_stream()
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    def tf(flop, ms):
+        return round(flop / (ms * 1e-3) / 1e12, 1)
+
+    out = {}
+    print("[bench] configs: forward 4096", file=sys.stderr, flush=True)
+    xb, wb = workloads.forward_4096()
+    x, w = to_dev(xb), to_dev(wb)
+    M, K = x.shape
+    N = w.shape[1]
+    lin = DelayedScalingLinear(hist_len=1024, device=dev)
+    lin.step(x, w)
+    step_ms = time_launches(torch, stream, lambda: lin.step(x, w), iters)
+    b, su = lin._bufs, lin.scale_used
+    g_ms = time_launches(torch, stream, lambda: fp8ds_gemm(
+        OP_N, OP_T, M, N, K, b["xq"], E4M3, K, su[0:1], b["wqt"], E4M3, K, su[1:2], b["y"], N,
+        lin.amax_y), iters)
+    out["forward_4096_m8192"] = {"step_ms": round(step_ms, 4), "gemm_ms": round(g_ms, 4),
+                                 "gemm_tflops": tf(2 * M * N * K, g_ms),
+                                 "gemm_frac_fp8_peak": round(tf(2 * M * N * K, g_ms) /
+                                                             PEAK_FP8_TFLOPS, 4)}
+    del x, w, lin, b
+    proj = {}
+    for name in ("q_proj", "k_proj", "gate_proj", "down_proj"):
+        print(f"[bench] configs: {name}", file=sys.stderr, flush=True)
+        xb, wb, dyb = workloads.llama_tensors(name, 0)
+        x, w, dy = to_dev(xb), to_dev(wb), to_dev(dyb)
+        M, K = x.shape
+        N = w.shape[1]
+        lin = DelayedScalingLinear(hist_len=16, device=dev)
+        lin.step(x, w, dy)
+        step_ms = time_launches(torch, stream, lambda: lin.step(x, w, dy), iters)
+        b, su = lin._bufs, lin.scale_used
+        calls = {
+            "fwd_nt": lambda: fp8ds_gemm(OP_N, OP_T, M, N, K, b["xq"], E4M3, K, su[0:1], b["wqt"],
+                                         E4M3, K, su[1:2], b["y"], N, lin.amax_y),
+            "dgrad_nt": lambda: fp8ds_gemm(OP_N, OP_T, M, K, N, b["dyq"], E5M2, N, su[2:3],
+                                           b["wq"], E4M3, N, su[1:2], b["dx"], K),
+            "wgrad_tn": lambda: fp8ds_gemm(OP_T, OP_N, K, N, M, b["xq"], E4M3, K, su[0:1],
+                                           b["dyq"], E5M2, N, su[2:3], b["dw"], N),
+        }
+        gem = {n: tf(2 * M * N * K, time_launches(torch, stream, fn, iters))
+               for n, fn in calls.items()}
+        proj[name] = {"M": M, "in": K, "out": N, "step_ms": round(step_ms, 4),
+                      "step_tflops": tf(6 * M * N * K, step_ms), "gemm_tflops": gem,
+                      "step_frac_fp8_peak": round(tf(6 * M * N * K, step_ms) / PEAK_FP8_TFLOPS, 4)}
+        del x, w, dy, lin, b
+    out["decoder_projections_m8192"] = proj
+    print("[bench] configs: 512 small Linears", file=sys.stderr, flush=True)
+    xb, wb = workloads.small_batch()
+    x, w = to_dev(xb), to_dev(wb)
+    B, M, K = x.shape
+    N = w.shape[2]
+    blin = BatchedDelayedScalingLinear(B, hist_len=16, device=dev)
+    blin.step(x, w)
+    ms = time_launches(torch, stream, lambda: blin.step(x, w), iters)
+    # bytes: casts read bf16 X, W (2 B) and write FP8 (1 B); the GEMM reads the FP8
+    # operands and writes bf16 Y
+    nbytes = B * (3 * (M * K + K * N) + (M * K + K * N) + 2 * M * N)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    out["small_batch_512x256"] = {"step_ms": round(ms, 4), "tflops": tf(2 * B * M * N * K, ms),
+                                  "GB/s": round(gbps, 1),
+                                  "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+    del x, w, blin
     torch.cuda.empty_cache()
     return out
 
@@ -330,6 +420,10 @@ def main():
 
     if not args.no_stress:
         result["cast_stress"] = stress_cast(torch, dsg, workloads, dev)
+    if not args.no_configs:
+        del sets, base
+        torch.cuda.empty_cache()
+        result["configs"] = configs_report(torch, dsg, workloads, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(xb, wb, dyb)
