@@ -290,9 +290,11 @@ __device__ __forceinline__ void transpose4x4_b(uint32_t i0, uint32_t i1, uint32_
   o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
-// Row tiles per workgroup (walked in sequence, one amax/saturation commit):
-// fewer workgroups meeting the freshly reset amax at once.
-constexpr int kTransposeTiles = 4;
+// Row tiles per workgroup (walked in sequence, one amax/saturation commit).
+#ifndef FP8DS_TRANSPOSE_TILES
+#define FP8DS_TRANSPOSE_TILES 1
+#endif
+constexpr int kTransposeTiles = FP8DS_TRANSPOSE_TILES;
 
 template <bool BF16, int FMT>
 __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restrict__ xp,
