@@ -539,7 +539,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
 
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
-  static_assert(!DIRECT || EXACT, "direct LDS loads are used by the exact datapath only");
   constexpr int NT = 256;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -609,6 +608,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     }
   };
 
+  // DIRECT: stages are loaded straight into LDS two stages ahead: stage k + 2
+  // goes into the buffer of stage k right after stage k's barrier (all waves
+  // have read it by then), and that barrier's wait on outstanding loads makes
+  // stage k + 1 complete before it is read.
+  auto issue_direct = [&](int kt, int buf) {
+    if constexpr (DIRECT) {
+      if constexpr (A_KC)
+        LoaderKCDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
+      else
+        LoaderMNDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
+      if constexpr (B_KC)
+        LoaderKCDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
+      else
+        LoaderMNDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
+    }
+  };
   if constexpr (EXACT) {
     u32x4 ra[2][FM], rb[2][FN];      // raw chunks, by unit parity
     u32x2 ha[2][FM][2], hb[2][FN][2]; // F16 operands of a step (8 values = 2 x u32x2), by step parity
@@ -643,22 +658,6 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       }
     };
 
-    // DIRECT: stages are loaded straight into LDS two stages ahead: stage k + 2
-    // goes into the buffer of stage k right after stage k's barrier (all waves
-    // have read it by then), and that barrier's wait on outstanding loads makes
-    // stage k + 1 complete before it is read.
-    auto issue_direct = [&](int kt, int buf) {
-      if constexpr (DIRECT) {
-        if constexpr (A_KC)
-          LoaderKCDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
-        else
-          LoaderMNDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
-        if constexpr (B_KC)
-          LoaderKCDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
-        else
-          LoaderMNDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
-      }
-    };
     if (nk > 0) {
       if constexpr (DIRECT) {
         issue_direct(0, 0);
@@ -720,17 +719,41 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     if (nk > 0) stage(nk - 1, std::false_type{});
   } else {
     u32x4 ra[2][FM][2], rb[2][FN][2];  // two chunks per step, by step parity
+    // Step s of a stage takes, per lane, 32 consecutive K values of its row:
+    // k = 64 (l / 32) + 32 s + [0, 32).  K-major tiles give them as two 16-byte
+    // chunks; MN-major tiles (direct loads of MN-contiguous operands) as four
+    // transposing 8-byte reads.
+    auto read_mn32 = [&](const uint8_t* tile, auto rows_tag, int r0, int s, u32x4 (&x)[2]) {
+      constexpr int R = decltype(rows_tag)::value;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x2 lo = ds_read_tr8(tile + mn_off<R>(tr_k + 32 * s + 16 * h, r0 + tr_row));
+        const u32x2 hi = ds_read_tr8(tile + mn_off<R>(tr_k + 32 * s + 16 * h + 8, r0 + tr_row));
+        x[h] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    };
     auto read_step = [&](int buf, int s, u32x4 (&xa)[FM][2], u32x4 (&xb)[FN][2]) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (B_MN_LDS) {
+          read_mn32(lds_b[buf], std::integral_constant<int, BN>{}, wn * WTN + j * 32, s, xb[j]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          xb[j][t] = *reinterpret_cast<const u32x4*>(
-              lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, fc + 2 * s + t));
+          for (int t = 0; t < 2; ++t)
+            xb[j][t] = *reinterpret_cast<const u32x4*>(
+                lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, fc + 2 * s + t));
+        }
+      }
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          xa[i][t] = *reinterpret_cast<const u32x4*>(
-              lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, fc + 2 * s + t));
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (A_MN_LDS) {
+          read_mn32(lds_a[buf], std::integral_constant<int, BM>{}, wm * WTM + i * 32, s, xa[i]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            xa[i][t] = *reinterpret_cast<const u32x4*>(
+                lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, fc + 2 * s + t));
+        }
       }
     };
     auto mma = [&](const u32x4 (&xa)[FM][2], const u32x4 (&xb)[FN][2]) {
@@ -749,29 +772,39 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       }
     };
     if (nk > 0) {
-      la.load(A, p.lda, m0, M, 0, K, tid);
-      lb.load(B, p.ldb, n0, N, 0, K, tid);
-      la.store(lds_a[0], tid);
-      lb.store(lds_b[0], tid);
+      if constexpr (DIRECT) {
+        issue_direct(0, 0);
+        if (nk > 1) issue_direct(1, 1);
+        vmem_wait_all();
+      } else {
+        la.load(A, p.lda, m0, M, 0, K, tid);
+        lb.load(B, p.ldb, n0, N, 0, K, tid);
+        la.store(lds_a[0], tid);
+        lb.store(lds_b[0], tid);
+      }
       __syncthreads();
       read_step(0, 0, ra[0], rb[0]);
     }
     auto stage = [&](int kt, auto more_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
       const int cur = kt & 1;
-      if constexpr (MORE) {
+      if constexpr (MORE && !DIRECT) {
         la.load(A, p.lda, m0, M, (int64_t)(kt + 1) * KB, K, tid);
         lb.load(B, p.ldb, n0, N, (int64_t)(kt + 1) * KB, K, tid);
       }
       read_step(cur, 1, ra[1], rb[1]);
-      if constexpr (MORE) {
+      if constexpr (MORE && !DIRECT) {
         la.store(lds_a[cur ^ 1], tid);
         lb.store(lds_b[cur ^ 1], tid);
       }
       mma(ra[0], rb[0]);
       if constexpr (MORE) {
+        if constexpr (DIRECT) vmem_wait_all();
         __syncthreads();
         read_step(cur ^ 1, 0, ra[0], rb[0]);
+        if constexpr (DIRECT) {
+          if (kt + 2 < nk) issue_direct(kt + 2, cur);
+        }
       }
       mma(ra[1], rb[1]);
     };
@@ -802,10 +835,10 @@ static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
 }
 
 // K a multiple of the stage depth and operands in aligned 16-byte chunks: LDS is
-// filled by direct loads (EXACT datapath); otherwise through registers.
+// filled by direct loads; otherwise through registers.
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT>
 static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream) {
-  if constexpr (EXACT) {
+  {
     // Direct loads move aligned 16-byte chunks; MN-contiguous operands are
     // loaded in whole chunks along M / N.
     auto aligned = [&](const uint8_t* ptr, int64_t ld, int64_t stride) {
