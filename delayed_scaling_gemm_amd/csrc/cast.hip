@@ -20,6 +20,7 @@ namespace fp8ds {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ prologue
 // Resets the reduction outputs and snapshots the scale, so the main kernels only
@@ -269,25 +270,22 @@ __global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastAr
 //   * each thread converts four 16-element row pieces (16-byte loads), stores the
 //     16 codes of each to q with one 16-byte store and parks them in an LDS tile
 //     of 128-byte rows;
-//   * after a barrier each thread reads a 16-row x 4-column block of codes as 16
-//     dwords (32 lanes read one whole LDS row: no bank conflicts), transposes it
-//     in registers with byte permutes and stores four 16-byte pieces of q_t
-//     (16 consecutive rows of one input column each).
+//   * the LDS rows hold 8-byte column groups XOR-swizzled by (row % 8); after a
+//     barrier, gfx950's transposing LDS read (ds_read_b64_tr_b8: within 16
+//     lanes, lane i receives byte i % 8 of the 8-byte pieces addressed by lanes
+//     2j + i / 8, j = 0..7) hands each lane 8 rows of one input column; two
+//     such reads give 16 rows, one 16-byte piece of q_t.  The four 16-lane
+//     groups of a wave take consecutive 16-row blocks of the same 16 columns,
+//     so each store instruction writes 64-byte runs of 16 q_t rows.  The
+//     swizzle puts the 16 pieces of a group's read in distinct banks.
 // Other tiles (ragged edges, unaligned shapes) convert element by element.
 
-__device__ __forceinline__ void transpose4x4_b(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t i3,
-                                               uint32_t& o0, uint32_t& o1, uint32_t& o2,
-                                               uint32_t& o3) {
-  // __builtin_amdgcn_perm(hi, lo, sel): byte i of the result is byte sel.byte_i of
-  // hi:lo (selector 0..3 = lo bytes, 4..7 = hi bytes); out[b] = byte b of i0..i3.
-  const uint32_t t0 = __builtin_amdgcn_perm(i1, i0, 0x05010400u);
-  const uint32_t t1 = __builtin_amdgcn_perm(i1, i0, 0x07030602u);
-  const uint32_t t2 = __builtin_amdgcn_perm(i3, i2, 0x05010400u);
-  const uint32_t t3 = __builtin_amdgcn_perm(i3, i2, 0x07030602u);
-  o0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  o1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  o2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+// gfx950 transposing LDS read of 8 bytes (ds_read_b64_tr_b8).
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  const v2i_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) v2i_t*)(p));
+  return u32x2{(uint32_t)v[0], (uint32_t)v[1]};
 }
 
 // Row tiles per workgroup (walked in sequence, one amax/saturation commit).
@@ -343,26 +341,30 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restr
           codes = cast16_f32<FMT>(d, s, amax, sat, g_sat != nullptr);
         }
         *reinterpret_cast<u32x4*>(q + off) = codes;
-        *reinterpret_cast<u32x4*>(tile + r * T + cp) = codes;
+        const int c8 = cp >> 3, sw = r & 7;  // two 8-byte column groups, swizzled
+        *reinterpret_cast<u32x2*>(tile + r * T + ((c8 ^ sw) << 3)) = u32x2{codes.x, codes.y};
+        *reinterpret_cast<u32x2*>(tile + r * T + (((c8 + 1) ^ sw) << 3)) = u32x2{codes.z, codes.w};
       }
       __syncthreads();
       {
-        const int cb = tid & 31;  // 4-column block
-        const int rb = tid >> 5;  // 16-row block
-        uint32_t w[16];
+        const int lane = tid & 63, wv = tid >> 6;
+        const int grp = lane >> 4, li = lane & 15;
+        const int j = li >> 1, hh = li & 1;  // as addresser: row + j, column group + hh
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          w[j] = *reinterpret_cast<const uint32_t*>(tile + (rb * 16 + j) * T + cb * 4);
-        uint32_t col[4][4];  // col[c][g]: rows 4g..4g+3 of column 4 cb + c
+        for (int it = 0; it < 4; ++it) {
+          const int cg = 2 * wv + (it >> 1);   // 16-column group of the tile
+          const int rb = 4 * (it & 1) + grp;   // 16-row block
+          u32x2 part[2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          transpose4x4_b(w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3], col[0][g], col[1][g],
-                         col[2][g], col[3][g]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int64_t oc = c0 + cb * 4 + c;
+          for (int half = 0; half < 2; ++half) {
+            const int r = rb * 16 + 8 * half + j;
+            const int c8 = 2 * cg + hh;
+            part[half] = lds_read_tr8(tile + r * T + ((c8 ^ (r & 7)) << 3));
+          }
+          // lane li holds column 16 cg + li, rows 16 rb .. 16 rb + 15
+          const int64_t oc = c0 + cg * 16 + li;
           *reinterpret_cast<u32x4*>(qt + oc * rows + r0 + rb * 16) =
-              u32x4{col[c][0], col[c][1], col[c][2], col[c][3]};
+              u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
         }
       }
     } else {
