@@ -20,7 +20,7 @@ casts (`cast_stress`), and `configs`, the throughput of the other workloads
 (forward-only 4096 Linear at M = 8192, the decoder-layer projections at
 M = 8192, 512 small Linears).
 
-Prints one JSON line.  `--gpus N` with N > 1 is refused: this build measures
+Prints one JSON line.  `--gpus N` with N > 1 is refused: the benchmark measures
 one GPU.  `--copy-calib` only runs device copies of known size (the reference
 for the HBM byte counters, see profiles/).
 """
@@ -262,8 +262,8 @@ def configs_report(torch, dsg, workloads, dev, iters=5):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU only "
-              "(how the Linear would shard over several GPUs is described, not built)",
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library and this benchmark "
+              "run on one GPU only (sharding the Linear over several GPUs is not implemented)",
               file=sys.stderr)
         sys.exit(2)
 
