@@ -193,6 +193,10 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
     return fail(FP8DS_ERR_SHAPE, "%s: bad M/N/K %lld/%lld/%lld", who, (long long)M, (long long)N,
                 (long long)K);
   if (batch < 0 || batch > 65535) return fail(FP8DS_ERR_SHAPE, "%s: bad batch", who);
+  // the launch grid counts 128 x 128 output tiles in one dimension
+  if (((M + 127) / 128) * ((N + 127) / 128) >= lim)
+    return fail(FP8DS_ERR_SHAPE, "%s: M x N %lld x %lld has too many tiles", who, (long long)M,
+                (long long)N);
   if (M == 0 || N == 0 || batch == 0) {
     if (amax_c && batch > 0)
       return hip_status(fp8ds::launch_prologue(batch, nullptr, nullptr, amax_c, nullptr, stream),

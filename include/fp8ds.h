@@ -198,7 +198,8 @@ int fp8ds_scale_update(int n_tensors, int hist_len, float* history, int32_t* cur
  * with round-to-nearest-even to BF16 (ct = BF16) or no rounding (ct = F32).
  *
  *   opa, opb   (N,N), (N,T) or (T,N); (T,T) returns FP8DS_ERR_UNSUPPORTED.
- *   M, N, K    >= 0.  op(A) is M x K, op(B) is K x N, C is M x N.
+ *   M, N, K    >= 0 and < 2^31, with ceil(M/128) * ceil(N/128) < 2^31 (else
+ *              FP8DS_ERR_SHAPE).  op(A) is M x K, op(B) is K x N, C is M x N.
  *   A          device: opa == N: [M x K] with lda >= K;  opa == T: [K x M] with lda >= M.
  *   B          device: opb == N: [K x N] with ldb >= N;  opb == T: [N x K] with ldb >= K.
  *   fa, fb     formats of A and B, independently E4M3 or E5M2.

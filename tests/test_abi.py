@@ -86,4 +86,9 @@ def test_validation_errors_without_gpu():
     assert g(0, 0, 64, 64, 64, C=None) == -1
     assert g(0, 0, 64, 64, 64, mma=2) == -3
     assert g(0, 0, 64, 64, 66) == -4
+    # M x N whose 128 x 128 tile count does not fit the launch grid: shape error
+    # before any pointer is looked at
+    big = (1 << 31) - 1
+    assert L.fp8ds_gemm(0, 1, big, big, 16, p, 0, 16, p, p, 0, 16, p, p, 1, big, None, 0,
+                        None) == -2
     assert args
