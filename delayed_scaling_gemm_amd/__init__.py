@@ -103,6 +103,38 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _need(t, name, dtypes, n, contiguous=True):
+    """Raise unless ``t`` (a torch tensor; raw integer pointers and None are not
+    checked) is a CUDA tensor of one of ``dtypes`` with at least ``n`` elements
+    addressable from its data pointer: a contiguous tensor of ``n`` elements
+    when the C call reads it as a dense array, else enough storage past the
+    pointer for the matrices that the leading dimensions describe.  The C ABI
+    sees only pointers; this keeps a mis-sized or strided tensor from being read
+    or written past its end."""
+    if t is None or isinstance(t, int):
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a CUDA tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if contiguous:
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous tensor")
+        avail = t.numel()
+    else:  # addressed through leading dimensions: what the storage holds past data_ptr
+        avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if avail < n:
+        raise ValueError(f"{name}: {avail} elements reachable, at least {n} needed")
+
+
+def _span(rows, cols, ld, batch=1, stride=0):
+    """Elements addressed by ``batch`` row-major [rows x cols] matrices with
+    leading dimension ``ld``, ``stride`` elements apart (0 when empty)."""
+    if rows <= 0 or cols <= 0 or batch <= 0:
+        return 0
+    return (batch - 1) * stride + (rows - 1) * ld + cols
+
+
 def _dtype_code(t):
     import torch
 
@@ -115,13 +147,27 @@ def _dtype_code(t):
 
 def fp8ds_amax(x, amax, stream=None):
     """amax[0] = max |x| (fp32 device tensor of 1 element)."""
+    import torch
+
+    _need(x, "x", (torch.bfloat16, torch.float32), 0)
+    _need(amax, "amax", (torch.float32,), 1)
     _check(lib().fp8ds_amax(_ptr(x), _dtype_code(x), x.numel(), _ptr(amax), _stream(stream)))
 
 
 def fp8ds_cast(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_count=None,
                stream=None):
     """Fused amax + scaled saturating cast of ``x`` ([rows, cols] or 1-D) into ``q`` (uint8)."""
+    import torch
+
     rows, cols = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.numel())
+    f32 = (torch.float32,)
+    _need(x, "x", (torch.bfloat16, torch.float32), 0)
+    _need(q, "q", (torch.uint8,), rows * cols)
+    _need(q_t, "q_t", (torch.uint8,), rows * cols)
+    _need(scale, "scale", f32, 1)
+    _need(scale_used, "scale_used", f32, 1)
+    _need(amax, "amax", f32, 1)
+    _need(sat_count, "sat_count", (torch.int64,), 1)
     _check(lib().fp8ds_cast(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
                             _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(sat_count),
                             _stream(stream)))
@@ -129,8 +175,20 @@ def fp8ds_cast(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_count
 
 def fp8ds_cast_batched(x, fmt, scale, q, scale_used=None, amax=None, sat_count=None, stream=None):
     """Casts of ``x[b]`` (a [batch, ...] tensor) with per-tensor ``scale[b]`` into ``q[b]``."""
+    import torch
+
     batch = x.shape[0]
     n = x[0].numel() if batch else 0
+    if batch and not (x[0].is_contiguous() and q[0].is_contiguous()):
+        raise ValueError("x[b] and q[b] must be contiguous")
+    f32 = (torch.float32,)
+    _need(x, "x", (torch.bfloat16, torch.float32), _span(batch, n, x.stride(0) if batch else n),
+          contiguous=False)
+    _need(q, "q", (torch.uint8,), _span(batch, n, q.stride(0) if batch else n), contiguous=False)
+    _need(scale, "scale", f32, batch)
+    _need(scale_used, "scale_used", f32, batch)
+    _need(amax, "amax", f32, batch)
+    _need(sat_count, "sat_count", (torch.int64,), batch)
     _check(lib().fp8ds_cast_batched(_ptr(x), _dtype_code(x), batch, n,
                                     x.stride(0) if batch else n, fmt, _ptr(scale), _ptr(q),
                                     q.stride(0) if batch else n, _ptr(scale_used), _ptr(amax),
@@ -143,16 +201,50 @@ def fp8ds_scale_update(history, cursor, amax, fmts, algo, margin, scale, scale_i
 
     ``history`` is [n, L] fp32, ``cursor`` [n] int32, ``amax`` and ``scale`` [n] fp32,
     ``fmts`` a host sequence of n formats."""
+    import torch
+
     n, L = history.shape
-    arr = (ctypes.c_int * n)(*[int(f) for f in fmts])
+    if len(fmts) < n:
+        raise ValueError(f"fmts: {len(fmts)} formats for {n} tensors")
+    f32 = (torch.float32,)
+    _need(history, "history", f32, n * L)
+    _need(cursor, "cursor", (torch.int32,), n)
+    _need(amax, "amax", f32, n)
+    _need(scale, "scale", f32, n)
+    _need(scale_inv, "scale_inv", f32, n)
+    arr = (ctypes.c_int * n)(*[int(f) for f in fmts[:n]])
     _check(lib().fp8ds_scale_update(n, L, _ptr(history), _ptr(cursor), _ptr(amax),
                                     ctypes.cast(arr, ctypes.c_void_p), algo, margin, _ptr(scale),
                                     _ptr(scale_inv), _stream(stream)))
 
 
+def _check_gemm(opa, opb, M, N, K, batch, a, lda, stride_a, scale_a, b, ldb, stride_b, scale_b, c,
+                ldc, stride_c, amax_c):
+    """Tensor arguments cover the matrices the C call will address (the C ABI
+    itself validates the sizes, leading dimensions and alignment)."""
+    import torch
+
+    if min(M, N, K, batch) < 0:
+        return  # the C call reports the bad size
+    ra, ca = (M, K) if opa == OP_N else (K, M)
+    rb, cb = (K, N) if opb == OP_N else (N, K)
+    f32 = (torch.float32,)
+    _need(amax_c, "amax_c", f32, batch)
+    if M == 0 or N == 0 or batch == 0:
+        return  # nothing but the output amax is touched
+    if K > 0:
+        _need(a, "a", (torch.uint8,), _span(ra, ca, lda, batch, stride_a), contiguous=False)
+        _need(b, "b", (torch.uint8,), _span(rb, cb, ldb, batch, stride_b), contiguous=False)
+    _need(c, "c", (torch.bfloat16, torch.float32), _span(M, N, ldc, batch, stride_c),
+          contiguous=False)
+    _need(scale_a, "scale_a", f32, batch)
+    _need(scale_b, "scale_b", f32, batch)
+
+
 def fp8ds_gemm(opa, opb, M, N, K, a, fa, lda, scale_a, b, fb, ldb, scale_b, c, ldc, amax_c=None,
                stream=None, mma=MMA_EXACT):
     """``c = dequant(op(a) @ op(b))`` with FP32 accumulation; ``c`` is bf16 or fp32."""
+    _check_gemm(opa, opb, M, N, K, 1, a, lda, 0, scale_a, b, ldb, 0, scale_b, c, ldc, 0, amax_c)
     _check(lib().fp8ds_gemm(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_a), _ptr(b), fb, ldb,
                             _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c), mma,
                             _stream(stream)))
@@ -162,6 +254,8 @@ def fp8ds_gemm_batched(opa, opb, M, N, K, batch, a, fa, lda, stride_a, scale_a, 
                        stride_b, scale_b, c, ldc, stride_c, amax_c=None, stream=None,
                        mma=MMA_EXACT):
     """``batch`` GEMMs of one shape with per-problem scales and output amax."""
+    _check_gemm(opa, opb, M, N, K, batch, a, lda, stride_a, scale_a, b, ldb, stride_b, scale_b, c,
+                ldc, stride_c, amax_c)
     _check(lib().fp8ds_gemm_batched(opa, opb, M, N, K, batch, _ptr(a), fa, lda, stride_a,
                                     _ptr(scale_a), _ptr(b), fb, ldb, stride_b, _ptr(scale_b),
                                     _ptr(c), _dtype_code(c), ldc, stride_c, _ptr(amax_c), mma,
