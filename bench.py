@@ -150,7 +150,8 @@ def time_launches(torch, stream, fn, iters):
 
 
 def stress_cast(torch, dsg, workloads, dev, iters=10):
-    """Standalone amax+cast of 2^30 bf16 elements to E4M3 and E5M2 (3 B/element)."""
+    """Standalone amax+cast of 2^30 bf16 elements to E4M3 and E5M2 (3 B/element),
+    the E4M3 cast with its health counts, and the amax alone."""
     n = 1 << 30
     print("[bench] stress cast 2^30", file=sys.stderr, flush=True)
     bits = workloads.big_cast_input(n)
@@ -169,6 +170,14 @@ def stress_cast(torch, dsg, workloads, dev, iters=10):
         gbps = 3.0 * n / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
                      "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "saturated": int(sat.item())}
+    counts = torch.zeros(dsg.HEALTH_COUNTS, dtype=torch.int64, device=dev)
+    dsg.fp8ds_cast_health(x, dsg.E4M3, s, q, counts, amax=am)
+    ms = time_launches(torch, stream,
+                       lambda: dsg.fp8ds_cast_health(x, dsg.E4M3, s, q, counts, amax=am), iters)
+    gbps = 3.0 * n / (ms * 1e-3) / 1e9
+    out["e4m3_health"] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                          "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                          "counts": dict(zip(dsg.HEALTH_NAMES, counts.cpu().tolist()))}
     ms = time_launches(torch, stream, lambda: dsg.fp8ds_amax(x, am), iters)
     out["amax"] = {"ms": round(ms, 4), "GB/s": round(2.0 * n / (ms * 1e-3) / 1e9, 1),
                    "frac_hbm": round(2.0 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}

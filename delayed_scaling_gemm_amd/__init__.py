@@ -6,8 +6,8 @@ memory and streams) into the pointers and sizes of the C ABI declared in
 runs in the library's HIP kernels.  There is no fallback: if the library is not
 built or cannot be loaded, every call raises.
 
-Functions keep the C names: ``fp8ds_amax``, ``fp8ds_cast``, ``fp8ds_cast_batched``,
-``fp8ds_scale_update``, ``fp8ds_gemm``, ``fp8ds_gemm_batched``.
+Functions keep the C names: ``fp8ds_amax``, ``fp8ds_cast``, ``fp8ds_cast_health``,
+``fp8ds_cast_batched``, ``fp8ds_scale_update``, ``fp8ds_gemm``, ``fp8ds_gemm_batched``.
 """
 
 from __future__ import annotations
@@ -52,6 +52,8 @@ def _declare(lib):
     lib.fp8ds_amax.argtypes = [vp, i32, i64, vp, vp]
     lib.fp8ds_cast.restype = i32
     lib.fp8ds_cast.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.fp8ds_cast_health.restype = i32
+    lib.fp8ds_cast_health.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.fp8ds_cast_batched.restype = i32
     lib.fp8ds_cast_batched.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i64, vp, vp, vp, vp]
     lib.fp8ds_scale_update.restype = i32
@@ -171,6 +173,33 @@ def fp8ds_cast(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_count
     _check(lib().fp8ds_cast(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
                             _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(sat_count),
                             _stream(stream)))
+
+
+HEALTH_COUNTS = 5
+HEALTH_NAMES = ("saturated", "nan", "inf", "zero", "near_max")
+
+
+def fp8ds_cast_health(x, fmt, scale, q, counts, q_t=None, scale_used=None, amax=None,
+                      stream=None):
+    """``fp8ds_cast`` plus the health counts of the same pass into ``counts``
+    (int64 device tensor of ``HEALTH_COUNTS``: saturated, NaN inputs, infinite
+    inputs, zero codes, top-binade codes)."""
+    import torch
+
+    rows, cols = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.numel())
+    f32 = (torch.float32,)
+    _need(x, "x", (torch.bfloat16, torch.float32), 0)
+    _need(q, "q", (torch.uint8,), rows * cols)
+    _need(q_t, "q_t", (torch.uint8,), rows * cols)
+    _need(scale, "scale", f32, 1)
+    _need(scale_used, "scale_used", f32, 1)
+    _need(amax, "amax", f32, 1)
+    if counts is None:
+        raise ValueError("counts is required")
+    _need(counts, "counts", (torch.int64,), HEALTH_COUNTS)
+    _check(lib().fp8ds_cast_health(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
+                                   _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(counts),
+                                   _stream(stream)))
 
 
 def fp8ds_cast_batched(x, fmt, scale, q, scale_used=None, amax=None, sat_count=None, stream=None):

@@ -88,38 +88,56 @@ int fp8ds_amax(const void* x, fp8ds_dtype xt, int64_t n, float* amax, hipStream_
   hipError_t e = fp8ds::launch_prologue(1, nullptr, nullptr, amax, nullptr, stream);
   if (e == hipSuccess && n > 0)
     e = fp8ds::launch_cast(x, xt == FP8DS_BF16, 1, n, n, 0, nullptr, nullptr, 0, amax, nullptr,
-                           num_cus(), stream);
+                           nullptr, num_cus(), stream);
   return hip_status(e, "fp8ds_amax");
+}
+
+static int cast_common(const char* who, const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols,
+                       fp8ds_format fmt, const float* scale, uint8_t* q, uint8_t* q_t,
+                       float* scale_used, float* amax, uint64_t* sat_count, uint64_t* health,
+                       hipStream_t stream) {
+  if (!scale) return fail(FP8DS_ERR_NULL, "%s: scale is null", who);
+  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "%s: bad dtype %d", who, (int)xt);
+  if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "%s: bad format %d", who, (int)fmt);
+  if (rows < 0 || cols < 0 || (cols > 0 && rows > kMaxElems / cols))
+    return fail(FP8DS_ERR_SHAPE, "%s: bad shape %lld x %lld", who, (long long)rows,
+                (long long)cols);
+  const int64_t n = rows * cols;
+  if (n > 0) {
+    if (!x || !q) return fail(FP8DS_ERR_NULL, "%s: x or q is null", who);
+    if (!aligned16(x) || !aligned16(q) || (q_t && !aligned16(q_t)))
+      return fail(FP8DS_ERR_ALIGN, "%s: x, q and q_t must be 16-byte aligned", who);
+  }
+  if (q_t && (rows + 127) / 128 > 65535)
+    return fail(FP8DS_ERR_SHAPE, "%s: a transposed copy supports at most %d rows", who,
+                65535 * 128);
+  // with health counts, sat_count is counts[0] and the four others follow it
+  hipError_t e = fp8ds::launch_prologue(1, scale, scale_used, amax, sat_count, stream,
+                                        health ? FP8DS_HEALTH_COUNTS : 1);
+  if (e == hipSuccess && n > 0) {
+    if (q_t)
+      e = fp8ds::launch_cast_transpose(x, xt == FP8DS_BF16, rows, cols, (int)fmt, scale, q, q_t,
+                                       amax, sat_count, health, stream);
+    else
+      e = fp8ds::launch_cast(x, xt == FP8DS_BF16, 1, n, n, (int)fmt, scale, q, n, amax, sat_count,
+                             health, num_cus(), stream);
+  }
+  return hip_status(e, who);
 }
 
 int fp8ds_cast(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
                const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
                uint64_t* sat_count, hipStream_t stream) {
-  if (!scale) return fail(FP8DS_ERR_NULL, "fp8ds_cast: scale is null");
-  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "fp8ds_cast: bad dtype %d", (int)xt);
-  if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "fp8ds_cast: bad format %d", (int)fmt);
-  if (rows < 0 || cols < 0 || (cols > 0 && rows > kMaxElems / cols))
-    return fail(FP8DS_ERR_SHAPE, "fp8ds_cast: bad shape %lld x %lld", (long long)rows,
-                (long long)cols);
-  const int64_t n = rows * cols;
-  if (n > 0) {
-    if (!x || !q) return fail(FP8DS_ERR_NULL, "fp8ds_cast: x or q is null");
-    if (!aligned16(x) || !aligned16(q) || (q_t && !aligned16(q_t)))
-      return fail(FP8DS_ERR_ALIGN, "fp8ds_cast: x, q and q_t must be 16-byte aligned");
-  }
-  if (q_t && (rows + 127) / 128 > 65535)
-    return fail(FP8DS_ERR_SHAPE, "fp8ds_cast: a transposed copy supports at most %d rows",
-                65535 * 128);
-  hipError_t e = fp8ds::launch_prologue(1, scale, scale_used, amax, sat_count, stream);
-  if (e == hipSuccess && n > 0) {
-    if (q_t)
-      e = fp8ds::launch_cast_transpose(x, xt == FP8DS_BF16, rows, cols, (int)fmt, scale, q, q_t,
-                                       amax, sat_count, stream);
-    else
-      e = fp8ds::launch_cast(x, xt == FP8DS_BF16, 1, n, n, (int)fmt, scale, q, n, amax, sat_count,
-                             num_cus(), stream);
-  }
-  return hip_status(e, "fp8ds_cast");
+  return cast_common("fp8ds_cast", x, xt, rows, cols, fmt, scale, q, q_t, scale_used, amax,
+                     sat_count, nullptr, stream);
+}
+
+int fp8ds_cast_health(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+                      const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
+                      uint64_t* counts, hipStream_t stream) {
+  if (!counts) return fail(FP8DS_ERR_NULL, "fp8ds_cast_health: counts is null");
+  return cast_common("fp8ds_cast_health", x, xt, rows, cols, fmt, scale, q, q_t, scale_used, amax,
+                     counts, counts + 1, stream);
 }
 
 int fp8ds_cast_batched(const void* x, fp8ds_dtype xt, int64_t batch, int64_t n, int64_t stride_x,
@@ -144,7 +162,7 @@ int fp8ds_cast_batched(const void* x, fp8ds_dtype xt, int64_t batch, int64_t n, 
   hipError_t e = fp8ds::launch_prologue(batch, scale, scale_used, amax, sat_count, stream);
   if (e == hipSuccess && n > 0)
     e = fp8ds::launch_cast(x, xt == FP8DS_BF16, batch, n, stride_x, (int)fmt, scale, q, stride_q,
-                           amax, sat_count, num_cus(), stream);
+                           amax, sat_count, nullptr, num_cus(), stream);
   return hip_status(e, "fp8ds_cast_batched");
 }
 

@@ -28,12 +28,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // captured into a graph.
 __global__ void prologue_kernel(int64_t count, const float* __restrict__ scale,
                                 float* __restrict__ scale_used, uint32_t* __restrict__ amax_bits,
-                                unsigned long long* __restrict__ sat) {
+                                unsigned long long* __restrict__ sat, int nc) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
   if (scale_used) scale_used[i] = scale[i];
   if (amax_bits) amax_bits[i] = 0u;
-  if (sat) sat[i] = 0ull;
+  if (sat)
+    for (int k = 0; k < nc; ++k) sat[i * nc + k] = 0ull;
 }
 
 // ------------------------------------------------------------------ element access
@@ -80,13 +81,52 @@ __device__ __forceinline__ uint32_t sat4(float a, float b, float c, float d) {
          (uint32_t)(fabsf(d) > M);
 }
 
+// Quantization-health counts of one thread: NaN and infinite inputs, zero
+// codes (+-0) and codes in the format's top binade [2^emax, max] (magnitude
+// byte 0x78 up to the largest finite code in both formats).
+struct Health {
+  uint32_t nan = 0, inf = 0, zero = 0, near = 0;
+};
+// largest finite code magnitude: 0x7E (448) in E4M3, 0x7B (57344) in E5M2
+template <int FMT>
+constexpr uint32_t max_code() { return FMT == kE4M3 ? 0x7Eu : 0x7Bu; }
+
+// Four codes in a dword: the byte tests are carry-free because every masked
+// byte is at most 0x7F.
+template <int FMT>
+__device__ __forceinline__ void health_codes(uint32_t c, Health& h) {
+  constexpr uint32_t kMaxCode = max_code<FMT>();
+  const uint32_t t = c & 0x7F7F7F7Fu;
+  const uint32_t nonzero = ((t + 0x7F7F7F7Fu) | t) & 0x80808080u;      // byte >= 1
+  const uint32_t ge = (t + 0x08080808u) & 0x80808080u;                 // byte >= 0x78
+  const uint32_t le = ((0x80808080u + kMaxCode * 0x01010101u) - t) & 0x80808080u;  // <= max
+  h.zero += 4u - (uint32_t)__builtin_popcount(nonzero);
+  h.near += (uint32_t)__builtin_popcount(ge & le);
+}
+template <int FMT>
+__device__ __forceinline__ void health_code1(uint32_t code, Health& h) {
+  const uint32_t m = code & 0x7Fu;
+  h.zero += (uint32_t)(m == 0u);
+  h.near += (uint32_t)(m >= 0x78u && m <= max_code<FMT>());
+}
+__device__ __forceinline__ void health_bf16_pair(uint32_t d, Health& h) {
+  const uint32_t lo = d & 0x7FFFu, hi = (d >> 16) & 0x7FFFu;
+  h.nan += (uint32_t)(lo > 0x7F80u) + (uint32_t)(hi > 0x7F80u);
+  h.inf += (uint32_t)(lo == 0x7F80u) + (uint32_t)(hi == 0x7F80u);
+}
+__device__ __forceinline__ void health_f32(uint32_t d, Health& h) {
+  const uint32_t m = d & 0x7FFFFFFFu;
+  h.nan += (uint32_t)(m > 0x7F800000u);
+  h.inf += (uint32_t)(m == 0x7F800000u);
+}
+
 // Process 16 consecutive elements already loaded as 8 dwords of bf16 pairs or 16
 // floats.  Returns the 16 codes; accumulates amax bits and saturations.  The
 // group's largest magnitude (needed for amax anyway) tells whether any element
 // is NaN; only such groups take the software encoder.
-template <int FMT>
+template <int FMT, bool STATS = false>
 __device__ __forceinline__ u32x4 cast16_bf16(const uint32_t (&d)[8], float s, u16x2& amax2,
-                                              uint32_t& sat, bool want_sat) {
+                                              uint32_t& sat, bool want_sat, Health* h = nullptr) {
   u16x2 gm = {0, 0};
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -102,12 +142,20 @@ __device__ __forceinline__ u32x4 cast16_bf16(const uint32_t (&d)[8], float s, u1
     out[j] = nan ? encode4_sw<FMT>(a, b, c, e) : encode4_hw<FMT>(a, b, c, e);
     if (want_sat) sat += sat4<FMT>(a, b, c, e);
   }
+  if constexpr (STATS) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) health_codes<FMT>(out[j], *h);
+    if (gm.x >= 0x7F80u || gm.y >= 0x7F80u) {  // some NaN or infinity in the group
+#pragma unroll
+      for (int j = 0; j < 8; ++j) health_bf16_pair(d[j], *h);
+    }
+  }
   return out;
 }
 
-template <int FMT>
+template <int FMT, bool STATS = false>
 __device__ __forceinline__ u32x4 cast16_f32(const uint32_t (&d)[16], float s, uint32_t& amax,
-                                             uint32_t& sat, bool want_sat) {
+                                             uint32_t& sat, bool want_sat, Health* h = nullptr) {
   uint32_t gm = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) gm = max(gm, d[i] & 0x7FFFFFFFu);
@@ -122,7 +170,37 @@ __device__ __forceinline__ u32x4 cast16_f32(const uint32_t (&d)[16], float s, ui
     out[j] = nan ? encode4_sw<FMT>(v[0], v[1], v[2], v[3]) : encode4_hw<FMT>(v[0], v[1], v[2], v[3]);
     if (want_sat) sat += sat4<FMT>(v[0], v[1], v[2], v[3]);
   }
+  if constexpr (STATS) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) health_codes<FMT>(out[j], *h);
+    if (gm >= 0x7F800000u) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) health_f32(d[i], *h);
+    }
+  }
   return out;
+}
+
+// Sums the workgroup's health counts into g[0..3] (NaN, Inf, zero, near-max):
+// wave sums, LDS (4 words per wave from `smem`), one atomic per nonzero count.
+__device__ __forceinline__ void block_commit_health(const Health& h, unsigned long long* g,
+                                                    uint32_t* smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t v[4] = {h.nan, h.inf, h.zero, h.near};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = wave_sum_u32(v[k]);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) smem[k * nw + wave] = v[k];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 0; k < 4; ++k) {
+      uint32_t t = 0;
+      for (int w = 0; w < nw; ++w) t += smem[k * nw + w];
+      if (t) atomicAdd(g + k, (unsigned long long)t);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ cast kernel
@@ -138,6 +216,7 @@ struct CastArgs {
   int64_t stride_q;   // bytes between tensors
   uint32_t* amax;     // [batch] or null
   unsigned long long* sat;  // [batch] or null
+  unsigned long long* health;  // [batch][4] NaN, Inf, zero, near-max counts (STATS)
 };
 
 // Groups of 16 elements per thread per launch: each workgroup of T threads owns
@@ -162,11 +241,12 @@ struct CastGroups {
   static constexpr int kThreads = FP8DS_CAST_THREADS;  // threads per workgroup
 };
 
-template <bool BF16, int FMT, bool WRITE_Q>
+template <bool BF16, int FMT, bool WRITE_Q, bool STATS>
 __global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastArgs p) {
   constexpr int G = CastGroups<BF16>::kGroups;
   constexpr int T = CastGroups<BF16>::kThreads;
-  __shared__ uint32_t red[2 * (T / 64)];
+  __shared__ uint32_t red[(STATS ? 6 : 2) * (T / 64)];
+  Health h;
   const int b = blockIdx.y;
   const float s = WRITE_Q ? p.scale[b] : 1.0f;
   const bool want_sat = WRITE_Q && p.sat != nullptr;
@@ -196,7 +276,7 @@ __global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastAr
         const uint32_t d[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w,
                                v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
         if constexpr (WRITE_Q) {
-          const u32x4 c = cast16_bf16<FMT>(d, s, amax2, sat, want_sat);
+          const u32x4 c = cast16_bf16<FMT, STATS>(d, s, amax2, sat, want_sat, &h);
           __builtin_nontemporal_store(c, reinterpret_cast<u32x4*>(q) + g);
         } else {
 #pragma unroll
@@ -212,8 +292,13 @@ __global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastAr
       amax = max(amax, (bits & 0x7FFFu) << 16);
       if constexpr (WRITE_Q) {
         const float vv = __uint_as_float(bits << 16) * s;
-        q[t0 + threadIdx.x] = (uint8_t)encode_fp8<FMT>(vv);
+        const uint32_t code = encode_fp8<FMT>(vv);
+        q[t0 + threadIdx.x] = (uint8_t)code;
         if (want_sat) sat += (uint32_t)(fabsf(vv) > FmtTraits<FMT>::kMax);
+        if constexpr (STATS) {
+          health_code1<FMT>(code, h);
+          health_bf16_pair(bits, h);
+        }
       }
     }
     amax = max(amax, ((uint32_t)max(amax2.x, amax2.y)) << 16);
@@ -241,7 +326,7 @@ __global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastAr
           d[4 * i + 3] = v[k][i].w;
         }
         if constexpr (WRITE_Q) {
-          const u32x4 c = cast16_f32<FMT>(d, s, amax, sat, want_sat);
+          const u32x4 c = cast16_f32<FMT, STATS>(d, s, amax, sat, want_sat, &h);
           __builtin_nontemporal_store(c, reinterpret_cast<u32x4*>(q) + g);
         } else {
 #pragma unroll
@@ -255,13 +340,19 @@ __global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastAr
       amax = max(amax, bits & 0x7FFFFFFFu);
       if constexpr (WRITE_Q) {
         const float vv = __uint_as_float(bits) * s;
-        q[t0 + threadIdx.x] = (uint8_t)encode_fp8<FMT>(vv);
+        const uint32_t code = encode_fp8<FMT>(vv);
+        q[t0 + threadIdx.x] = (uint8_t)code;
         if (want_sat) sat += (uint32_t)(fabsf(vv) > FmtTraits<FMT>::kMax);
+        if constexpr (STATS) {
+          health_code1<FMT>(code, h);
+          health_f32(bits, h);
+        }
       }
     }
   }
   block_commit_amax_sat(amax, sat, p.amax ? p.amax + b : nullptr, want_sat ? p.sat + b : nullptr,
                         red);
+  if constexpr (STATS) block_commit_health(h, p.health + 4 * b, red + 2 * (T / 64));
 }
 
 // ------------------------------------------------------------------ cast + transposed copy
@@ -294,17 +385,15 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
 #endif
 constexpr int kTransposeTiles = FP8DS_TRANSPOSE_TILES;
 
-template <bool BF16, int FMT>
-__global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restrict__ xp,
-                                                             int64_t rows, int64_t cols,
-                                                             const float* __restrict__ scale,
-                                                             uint8_t* __restrict__ q,
-                                                             uint8_t* __restrict__ qt,
-                                                             uint32_t* __restrict__ g_amax,
-                                                             unsigned long long* __restrict__ g_sat) {
+template <bool BF16, int FMT, bool STATS>
+__global__ __launch_bounds__(256) void cast_transpose_kernel(
+    const void* __restrict__ xp, int64_t rows, int64_t cols, const float* __restrict__ scale,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ qt, uint32_t* __restrict__ g_amax,
+    unsigned long long* __restrict__ g_sat, unsigned long long* __restrict__ g_health) {
   constexpr int T = 128;
   __shared__ __attribute__((aligned(16))) uint8_t tile[T * T];
-  __shared__ uint32_t red[8];
+  __shared__ uint32_t red[(STATS ? 6 : 2) * 4];
+  Health h;
   const float s = scale[0];
   const int64_t c0 = (int64_t)blockIdx.x * T;
   const int tid = threadIdx.x;
@@ -328,7 +417,7 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restr
           const u32x4 v0 = src[0], v1 = src[1];
           const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
           u16x2 amax2 = {0, 0};
-          codes = cast16_bf16<FMT>(d, s, amax2, sat, g_sat != nullptr);
+          codes = cast16_bf16<FMT, STATS>(d, s, amax2, sat, g_sat != nullptr, &h);
           amax = max(amax, ((uint32_t)max(amax2.x, amax2.y)) << 16);
         } else {
           const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(xp) + off);
@@ -338,7 +427,7 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restr
             const u32x4 v = src[k];
             d[4 * k] = v.x; d[4 * k + 1] = v.y; d[4 * k + 2] = v.z; d[4 * k + 3] = v.w;
           }
-          codes = cast16_f32<FMT>(d, s, amax, sat, g_sat != nullptr);
+          codes = cast16_f32<FMT, STATS>(d, s, amax, sat, g_sat != nullptr, &h);
         }
         *reinterpret_cast<u32x4*>(q + off) = codes;
         const int c8 = cp >> 3, sw = r & 7;  // two 8-byte column groups, swizzled
@@ -380,13 +469,16 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restr
             const uint32_t bits = static_cast<const uint16_t*>(xp)[r * cols + c];
             amax = max(amax, (bits & 0x7FFFu) << 16);
             v = __uint_as_float(bits << 16) * s;
+            if constexpr (STATS) health_bf16_pair(bits, h);
           } else {
             const uint32_t bits = static_cast<const uint32_t*>(xp)[r * cols + c];
             amax = max(amax, bits & 0x7FFFFFFFu);
             v = __uint_as_float(bits) * s;
+            if constexpr (STATS) health_f32(bits, h);
           }
           code = encode_fp8<FMT>(v);
           if (g_sat) sat += (uint32_t)(fabsf(v) > FmtTraits<FMT>::kMax);
+          if constexpr (STATS) health_code1<FMT>(code, h);
           q[r * cols + c] = (uint8_t)code;
         }
         tile[tr * T + tc + i] = (uint8_t)code;
@@ -404,72 +496,96 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const void* __restr
     }
   }
   block_commit_amax_sat(amax, sat, g_amax, g_sat, red);
+  if constexpr (STATS) block_commit_health(h, g_health, red + 8);
 }
 
 // ------------------------------------------------------------------ host launchers
 
 hipError_t launch_prologue(int64_t count, const float* scale, float* scale_used, float* amax,
-                           uint64_t* sat, hipStream_t stream) {
+                           uint64_t* sat, hipStream_t stream, int counters) {
   if (count <= 0 || (!scale_used && !amax && !sat)) return hipSuccess;
   int blocks = (int)((count + 255) / 256);
   hipLaunchKernelGGL(prologue_kernel, dim3(blocks), dim3(256), 0, stream, count, scale, scale_used,
-                     reinterpret_cast<uint32_t*>(amax), reinterpret_cast<unsigned long long*>(sat));
+                     reinterpret_cast<uint32_t*>(amax), reinterpret_cast<unsigned long long*>(sat),
+                     counters);
   return hipGetLastError();
 }
 
-template <bool BF16, int FMT, bool WRITE_Q>
-static hipError_t launch_cast_t(const CastArgs& a, int64_t batch, int num_cus, hipStream_t stream) {
-  (void)num_cus;
+template <bool BF16, int FMT, bool WRITE_Q, bool STATS>
+static hipError_t launch_cast_t(const CastArgs& a, int64_t batch, hipStream_t stream) {
   constexpr int64_t T = CastGroups<BF16>::kThreads;
   constexpr int64_t per_block = T * CastGroups<BF16>::kGroups;
   const int64_t groups = a.n >> 4;
   int64_t gx = (groups + per_block - 1) / per_block;
   if (gx < 1) gx = 1;  // block 0 also takes the ragged tail (fewer than 16 elements)
-  hipLaunchKernelGGL((cast_kernel<BF16, FMT, WRITE_Q>), dim3((unsigned)gx, (unsigned)batch),
+  hipLaunchKernelGGL((cast_kernel<BF16, FMT, WRITE_Q, STATS>), dim3((unsigned)gx, (unsigned)batch),
                      dim3((unsigned)T), 0, stream, a);
   return hipGetLastError();
 }
 
+template <bool BF16, bool STATS>
+static hipError_t launch_cast_f(const CastArgs& a, int fmt, int64_t batch, hipStream_t stream) {
+  return fmt == kE4M3 ? launch_cast_t<BF16, kE4M3, true, STATS>(a, batch, stream)
+                      : launch_cast_t<BF16, kE5M2, true, STATS>(a, batch, stream);
+}
+
 hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride_x,
                        int fmt, const float* scale, uint8_t* q, int64_t stride_q, float* amax,
-                       uint64_t* sat, int num_cus, hipStream_t stream) {
+                       uint64_t* sat, uint64_t* health, int num_cus, hipStream_t stream) {
+  (void)num_cus;
   CastArgs a{x, n, stride_x, scale, q, stride_q, reinterpret_cast<uint32_t*>(amax),
-             reinterpret_cast<unsigned long long*>(sat)};
+             reinterpret_cast<unsigned long long*>(sat),
+             reinterpret_cast<unsigned long long*>(health)};
   if (q == nullptr) {
-    return bf16 ? launch_cast_t<true, kE4M3, false>(a, batch, num_cus, stream)
-                : launch_cast_t<false, kE4M3, false>(a, batch, num_cus, stream);
+    return bf16 ? launch_cast_t<true, kE4M3, false, false>(a, batch, stream)
+                : launch_cast_t<false, kE4M3, false, false>(a, batch, stream);
   }
-  if (bf16) {
-    return fmt == kE4M3 ? launch_cast_t<true, kE4M3, true>(a, batch, num_cus, stream)
-                        : launch_cast_t<true, kE5M2, true>(a, batch, num_cus, stream);
-  }
-  return fmt == kE4M3 ? launch_cast_t<false, kE4M3, true>(a, batch, num_cus, stream)
-                      : launch_cast_t<false, kE5M2, true>(a, batch, num_cus, stream);
+  if (health)
+    return bf16 ? launch_cast_f<true, true>(a, fmt, batch, stream)
+                : launch_cast_f<false, true>(a, fmt, batch, stream);
+  return bf16 ? launch_cast_f<true, false>(a, fmt, batch, stream)
+              : launch_cast_f<false, false>(a, fmt, batch, stream);
+}
+
+template <bool BF16, int FMT, bool STATS>
+static hipError_t launch_transpose_t(dim3 grid, const void* x, int64_t rows, int64_t cols,
+                                     const float* scale, uint8_t* q, uint8_t* qt, float* amax,
+                                     uint64_t* sat, uint64_t* health, hipStream_t stream) {
+  hipLaunchKernelGGL((cast_transpose_kernel<BF16, FMT, STATS>), grid, dim3(256), 0, stream, x,
+                     rows, cols, scale, q, qt, reinterpret_cast<uint32_t*>(amax),
+                     reinterpret_cast<unsigned long long*>(sat),
+                     reinterpret_cast<unsigned long long*>(health));
+  return hipGetLastError();
+}
+
+template <bool STATS>
+static hipError_t launch_transpose_s(dim3 grid, const void* x, bool bf16, int64_t rows,
+                                     int64_t cols, int fmt, const float* scale, uint8_t* q,
+                                     uint8_t* qt, float* amax, uint64_t* sat, uint64_t* health,
+                                     hipStream_t stream) {
+  if (bf16)
+    return fmt == kE4M3
+               ? launch_transpose_t<true, kE4M3, STATS>(grid, x, rows, cols, scale, q, qt, amax,
+                                                        sat, health, stream)
+               : launch_transpose_t<true, kE5M2, STATS>(grid, x, rows, cols, scale, q, qt, amax,
+                                                        sat, health, stream);
+  return fmt == kE4M3
+             ? launch_transpose_t<false, kE4M3, STATS>(grid, x, rows, cols, scale, q, qt, amax, sat,
+                                                       health, stream)
+             : launch_transpose_t<false, kE5M2, STATS>(grid, x, rows, cols, scale, q, qt, amax, sat,
+                                                       health, stream);
 }
 
 hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
                                  const float* scale, uint8_t* q, uint8_t* qt, float* amax,
-                                 uint64_t* sat, hipStream_t stream) {
+                                 uint64_t* sat, uint64_t* health, hipStream_t stream) {
   dim3 grid((unsigned)((cols + 127) / 128),
             (unsigned)(((rows + 127) / 128 + kTransposeTiles - 1) / kTransposeTiles));
-  uint32_t* am = reinterpret_cast<uint32_t*>(amax);
-  unsigned long long* st = reinterpret_cast<unsigned long long*>(sat);
-  if (bf16) {
-    if (fmt == kE4M3)
-      hipLaunchKernelGGL((cast_transpose_kernel<true, kE4M3>), grid, dim3(256), 0, stream, x, rows,
-                         cols, scale, q, qt, am, st);
-    else
-      hipLaunchKernelGGL((cast_transpose_kernel<true, kE5M2>), grid, dim3(256), 0, stream, x, rows,
-                         cols, scale, q, qt, am, st);
-  } else {
-    if (fmt == kE4M3)
-      hipLaunchKernelGGL((cast_transpose_kernel<false, kE4M3>), grid, dim3(256), 0, stream, x, rows,
-                         cols, scale, q, qt, am, st);
-    else
-      hipLaunchKernelGGL((cast_transpose_kernel<false, kE5M2>), grid, dim3(256), 0, stream, x, rows,
-                         cols, scale, q, qt, am, st);
-  }
-  return hipGetLastError();
+  if (health)
+    return launch_transpose_s<true>(grid, x, bf16, rows, cols, fmt, scale, q, qt, amax, sat,
+                                    health, stream);
+  return launch_transpose_s<false>(grid, x, bf16, rows, cols, fmt, scale, q, qt, amax, sat,
+                                   nullptr, stream);
 }
 
 }  // namespace fp8ds

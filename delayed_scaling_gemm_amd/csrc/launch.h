@@ -8,20 +8,22 @@
 
 namespace fp8ds {
 
-// scale_used[i] = scale[i]; amax[i] = 0; sat[i] = 0 for i < count (null outputs skipped).
+// scale_used[i] = scale[i]; amax[i] = 0; sat[i * counters + k] = 0 for k < counters,
+// i < count (null outputs skipped).
 hipError_t launch_prologue(int64_t count, const float* scale, float* scale_used, float* amax,
-                           uint64_t* sat, hipStream_t stream);
+                           uint64_t* sat, hipStream_t stream, int counters = 1);
 
 // Fused amax + cast over `batch` tensors of n elements (q == nullptr: amax only).
-// amax and sat must have been reset by launch_prologue.
+// amax, sat and health must have been reset by launch_prologue.  health (or null):
+// [batch][4] counts of NaN inputs, infinite inputs, zero codes and top-binade codes.
 hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride_x,
                        int fmt, const float* scale, uint8_t* q, int64_t stride_q, float* amax,
-                       uint64_t* sat, int num_cus, hipStream_t stream);
+                       uint64_t* sat, uint64_t* health, int num_cus, hipStream_t stream);
 
-// Cast of a [rows x cols] tensor writing q and its transpose qt.
+// Cast of a [rows x cols] tensor writing q and its transpose qt (health as above).
 hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
                                  const float* scale, uint8_t* q, uint8_t* qt, float* amax,
-                                 uint64_t* sat, hipStream_t stream);
+                                 uint64_t* sat, uint64_t* health, hipStream_t stream);
 
 // History push + window reduction + next scale for n tensors.
 // fmt_bits: bit t set = tensor t is E5M2.

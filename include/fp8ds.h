@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8DS_ABI_VERSION 2
+#define FP8DS_ABI_VERSION 3
 
 typedef enum {
   FP8DS_OK = 0,
@@ -140,6 +140,26 @@ int fp8ds_amax(const void* x, fp8ds_dtype xt, int64_t n, float* amax, hipStream_
 int fp8ds_cast(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
                const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
                uint64_t* sat_count, hipStream_t stream);
+
+/*
+ * fp8ds_cast_health -- fp8ds_cast plus quantization-health counts of the same pass.
+ * [P3] "第四步：建立 Amax 与低精度异常画像" (per-module metrics: the share of values
+ * near the FP8 upper limit, the share of zeros after quantization, NaN / Inf /
+ * overflow counts); [P2] §七 "陷阱 1：NaN/Inf 难以定位" (NaN and Inf checks).
+ *
+ * Arguments as fp8ds_cast, with sat_count replaced by
+ *   counts     device, FP8DS_HEALTH_COUNTS uint64 (required), reset by the call:
+ *              [0] saturated: #{|fl32(x*scale)| > max} (infinities counted, NaN not)
+ *              [1] NaN inputs
+ *              [2] infinite inputs
+ *              [3] zero codes: q[i] is +-0 (underflow to zero and exact zeros)
+ *              [4] near-max codes: q[i] finite with magnitude in the format's top
+ *                  binade [2^emax, max] ([256, 448] E4M3, [32768, 57344] E5M2).
+ */
+#define FP8DS_HEALTH_COUNTS 5
+int fp8ds_cast_health(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+                      const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
+                      uint64_t* counts, hipStream_t stream);
 
 /*
  * fp8ds_cast_batched -- `batch` independent casts of equal size n, each with its

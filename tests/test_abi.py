@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(dsg.LIB_PATH)
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert dsg.abi_version() == 2
+    assert dsg.abi_version() == 3
 
 
 def test_status_strings():
