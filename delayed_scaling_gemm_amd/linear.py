@@ -26,7 +26,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (ALGO_MAX, E4M3, E5M2, OP_N, OP_T, fp8ds_cast, fp8ds_gemm, fp8ds_scale_update)
+from . import (ALGO_MAX, E4M3, E5M2, HEALTH_COUNTS, HEALTH_NAMES, OP_N, OP_T, fp8ds_cast,
+               fp8ds_cast_health, fp8ds_gemm, fp8ds_scale_update)
 
 X, W, DY = 0, 1, 2
 
@@ -36,7 +37,8 @@ class DelayedScalingLinear:
     tensor X, W, dY) and its fwd(+bwd) step."""
 
     def __init__(self, hist_len: int = 16, algo: int = ALGO_MAX, margin: int = 0,
-                 fmts=(E4M3, E4M3, E5M2), device="cuda"):
+                 fmts=(E4M3, E4M3, E5M2), device="cuda", health: bool = False):
+        self.health = health
         self.hist_len = hist_len
         self.algo = algo
         self.margin = margin
@@ -50,7 +52,27 @@ class DelayedScalingLinear:
         self.amax = torch.zeros(3, **f32)
         self.sat = torch.zeros(3, dtype=torch.int64, device=self.device)
         self.amax_y = torch.zeros(1, **f32)
+        # health=True: each cast also counts saturated, NaN, Inf, zero and
+        # top-binade values (fp8ds_cast_health) into counts[X | W | DY]
+        self.counts = (torch.zeros(3, HEALTH_COUNTS, dtype=torch.int64, device=self.device)
+                       if health else None)
         self._bufs = {}
+
+    def _cast(self, t, x, q, q_t, stream):
+        s, su, am = self.scale, self.scale_used, self.amax
+        if self.health:
+            fp8ds_cast_health(x, self.fmts[t], s[t:t + 1], q, self.counts[t], q_t, su[t:t + 1],
+                              am[t:t + 1], stream)
+        else:
+            fp8ds_cast(x, self.fmts[t], s[t:t + 1], q, q_t, su[t:t + 1], am[t:t + 1],
+                       self.sat[t:t + 1], stream)
+
+    def health_report(self):
+        """Host copy of the last step's counts: {"x"|"w"|"dy": {name: count}} (synchronises)."""
+        if self.counts is None:
+            return None
+        c = self.counts.cpu().tolist()
+        return {k: dict(zip(HEALTH_NAMES, c[i])) for i, k in enumerate(("x", "w", "dy"))}
 
     def _buf(self, name, shape, dtype):
         t = self._bufs.get(name)
@@ -73,11 +95,9 @@ class DelayedScalingLinear:
         wq = self._buf("wq", (K, N), u8)
         wqt = self._buf("wqt", (N, K), u8)
         y = self._buf("y", (M, N), torch.bfloat16)
-        s, su, am, sat = self.scale, self.scale_used, self.amax, self.sat
-        fp8ds_cast(x, self.fmts[X], s[X:X + 1], xq, None, su[X:X + 1], am[X:X + 1], sat[X:X + 1],
-                   stream)
-        fp8ds_cast(w, self.fmts[W], s[W:W + 1], wq, wqt, su[W:W + 1], am[W:W + 1], sat[W:W + 1],
-                   stream)
+        s, su, am = self.scale, self.scale_used, self.amax
+        self._cast(X, x, xq, None, stream)
+        self._cast(W, w, wq, wqt, stream)
         # Y[M, N] = Xq[M, K] . Wq[K, N], with Wq^T stored [N, K] -> op T
         fp8ds_gemm(OP_N, OP_T, M, N, K, xq, self.fmts[X], K, su[X:X + 1], wqt, self.fmts[W], K,
                    su[W:W + 1], y, N, self.amax_y, stream)
@@ -88,8 +108,7 @@ class DelayedScalingLinear:
             dyq = self._buf("dyq", (M, N), u8)
             dx = self._buf("dx", (M, K), torch.bfloat16)
             dw = self._buf("dw", (K, N), torch.bfloat16)
-            fp8ds_cast(dy, self.fmts[DY], s[DY:DY + 1], dyq, None, su[DY:DY + 1], am[DY:DY + 1],
-                       sat[DY:DY + 1], stream)
+            self._cast(DY, dy, dyq, None, stream)
             # dX[M, K] = dYq[M, N] . Wq^T   (Wq stored [K, N] = [N' x K'] -> op T)
             fp8ds_gemm(OP_N, OP_T, M, K, N, dyq, self.fmts[DY], N, su[DY:DY + 1], wq, self.fmts[W],
                        N, su[W:W + 1], dx, K, None, stream)

@@ -140,3 +140,29 @@ def test_fwd_bwd_4096_full_size_sampled():
             states[name].update(oamax.amax(obf16.widen(bits)), 0, 0)
         compare_state(lin, states)
         print(f"[fwd_bwd_4096] step {step} ok", flush=True)
+
+
+def test_decoder_projection_health_counts():
+    """health=True on the k_proj trajectory (drift, 50x batch at step 6): each
+    step's counts for X, W and dY equal the oracle's for the cast with the
+    step's scale snapshot, and the codes are those of the plain step."""
+    from oracle import health as ohealth
+
+    M = 512
+    lin = DelayedScalingLinear(hist_len=16, algo=dsg.ALGO_MAX, margin=0, health=True)
+    states = oracle_states(16)
+    saw_saturation = False
+    for step in range(10):
+        xb, wb, dyb = workloads.llama_tensors("k_proj", step, m=M)
+        out = lin.step(dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb))
+        x, w, dy = obf16.widen(xb), obf16.widen(wb), obf16.widen(dyb)
+        ref = olinear.train_step(x, w, dy, states, dsg.ALGO_MAX, 0)
+        rep = lin.health_report()
+        for nm, ck, v in (("x", "cast_x", x), ("w", "cast_w", w), ("dy", "cast_dy", dy)):
+            c = ref[ck]
+            exp = ohealth.cast_health(v, c.scale_used, states[nm].fmt)
+            assert rep[nm] == exp, (step, nm, rep[nm], exp)
+            saw_saturation |= exp["saturated"] > 0
+        assert np.array_equal(out["xq"].cpu().numpy(), ref["cast_x"].codes)
+        compare_state(lin, states)
+    assert saw_saturation  # the 50x batch saturates X's cast
