@@ -85,6 +85,39 @@ class DelayedScalingLinear:
         """Copies of the scaling state (history, cursor, scale)."""
         return self.history.clone(), self.cursor.clone(), self.scale.clone()
 
+    # Checkpoint / resume ("LLM FP8 微调上线生产实战" §核心原理 "Delayed Scaling 用
+    # 历史换取稳定性": the scale of a step comes from the amax history; a restore
+    # that keeps the scale but drops the history changes the scales that follow).
+    # The state is exactly the recipe plus, per tensor, the history ring, its
+    # cursor and the current scale.
+
+    def state_dict(self) -> dict:
+        """Host copies of the scaling state and the recipe."""
+        return {"history": self.history.detach().cpu().clone(),
+                "cursor": self.cursor.detach().cpu().clone(),
+                "scale": self.scale.detach().cpu().clone(),
+                "recipe": torch.tensor([self.hist_len, self.algo, self.margin, *self.fmts],
+                                       dtype=torch.int64)}
+
+    def load_state_dict(self, d: dict):
+        """Restore a state saved by :meth:`state_dict` (the recipe must match)."""
+        recipe = [int(v) for v in d["recipe"].tolist()]
+        if recipe != [self.hist_len, self.algo, self.margin, *self.fmts]:
+            raise ValueError(f"recipe {recipe} does not match this Linear's "
+                             f"{[self.hist_len, self.algo, self.margin, *self.fmts]}")
+        for name in ("history", "cursor", "scale"):
+            src, dst = d[name], getattr(self, name)
+            if tuple(src.shape) != tuple(dst.shape) or src.dtype != dst.dtype:
+                raise ValueError(f"{name}: {tuple(src.shape)} {src.dtype} vs "
+                                 f"{tuple(dst.shape)} {dst.dtype}")
+            dst.copy_(src.to(dst.device))
+
+    def save(self, path: str):
+        torch.save(self.state_dict(), path)
+
+    def load(self, path: str):
+        self.load_state_dict(torch.load(path, map_location="cpu", weights_only=True))
+
     def step(self, x, w, dy=None, stream=None):
         """One step; returns a dict with the FP8 operands and the BF16 outputs."""
         M, K = x.shape

@@ -166,3 +166,46 @@ def test_decoder_projection_health_counts():
         assert np.array_equal(out["xq"].cpu().numpy(), ref["cast_x"].codes)
         compare_state(lin, states)
     assert saw_saturation  # the 50x batch saturates X's cast
+
+
+def test_checkpoint_resume_is_bit_identical(tmp_path):
+    """Save the scaling state after step 7 of the k_proj trajectory (the 50x batch
+    of step 6 is in every window), restore it into a fresh Linear and continue:
+    steps 8 and 9 reproduce the uninterrupted run bit for bit.  Restoring only
+    the scale (dropping the history) does not: the outlier leaves the window
+    early and the next scale changes, the pages' scale-mismatch incident."""
+    M = 256
+
+    def inputs(step):
+        xb, wb, dyb = workloads.llama_tensors("k_proj", step, m=M)
+        return dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb)
+
+    ref = DelayedScalingLinear(hist_len=16)
+    run = DelayedScalingLinear(hist_len=16)
+    outs = {}
+    for step in range(10):
+        o = ref.step(*inputs(step))
+        outs[step] = ({k: v.clone() for k, v in o.items()},
+                      {k: t.clone() for k, t in (("scale", ref.scale), ("amax", ref.amax),
+                                                 ("history", ref.history),
+                                                 ("cursor", ref.cursor))})
+        if step < 8:
+            run.step(*inputs(step))
+    path = str(tmp_path / "k_proj_scaling.pt")
+    run.save(path)
+    resumed = DelayedScalingLinear(hist_len=16)
+    resumed.load(path)
+    scale_only = DelayedScalingLinear(hist_len=16)
+    scale_only.scale.copy_(run.scale)
+    for step in (8, 9):
+        o = resumed.step(*inputs(step))
+        scale_only.step(*inputs(step))
+        torch.cuda.synchronize()
+        ro, rs = outs[step]
+        for k in ("xq", "wq", "wqt", "dyq"):
+            assert torch.equal(o[k], ro[k]), (step, k)
+        for k in ("y", "dx", "dw"):
+            assert torch.equal(o[k].view(torch.int16), ro[k].view(torch.int16)), (step, k)
+        for k in ("scale", "amax", "history", "cursor"):
+            assert torch.equal(getattr(resumed, k), rs[k]), (step, k)
+    assert not torch.equal(scale_only.scale, outs[9][1]["scale"])
