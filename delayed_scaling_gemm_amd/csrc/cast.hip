@@ -93,15 +93,36 @@ constexpr uint32_t max_code() { return FMT == kE4M3 ? 0x7Eu : 0x7Bu; }
 
 // Four codes in a dword: the byte tests are carry-free because every masked
 // byte is at most 0x7F.
+__device__ __forceinline__ void health_zero4(uint32_t c, Health& h) {
+  const uint32_t t = c & 0x7F7F7F7Fu;
+  const uint32_t nonzero = ((t + 0x7F7F7F7Fu) | t) & 0x80808080u;  // byte >= 1
+  h.zero += 4u - (uint32_t)__builtin_popcount(nonzero);
+}
 template <int FMT>
-__device__ __forceinline__ void health_codes(uint32_t c, Health& h) {
+__device__ __forceinline__ void health_near4(uint32_t c, Health& h) {
   constexpr uint32_t kMaxCode = max_code<FMT>();
   const uint32_t t = c & 0x7F7F7F7Fu;
-  const uint32_t nonzero = ((t + 0x7F7F7F7Fu) | t) & 0x80808080u;      // byte >= 1
-  const uint32_t ge = (t + 0x08080808u) & 0x80808080u;                 // byte >= 0x78
+  const uint32_t ge = (t + 0x08080808u) & 0x80808080u;                              // >= 0x78
   const uint32_t le = ((0x80808080u + kMaxCode * 0x01010101u) - t) & 0x80808080u;  // <= max
-  h.zero += 4u - (uint32_t)__builtin_popcount(nonzero);
   h.near += (uint32_t)__builtin_popcount(ge & le);
+}
+// A group can hold a zero code only if its smallest scaled magnitude is below
+// the smallest subnormal, and a top-binade code only if its largest reaches the
+// binade below (both tests are monotonic in |x|, so groups that fail them are
+// skipped exactly); groups with a NaN are always counted.
+template <int FMT>
+__device__ __forceinline__ void health_group(const u32x4& out, float lo, float hi, bool nan,
+                                             Health& h) {
+  constexpr float kMinSub = FMT == kE4M3 ? 0x1.0p-9f : 0x1.0p-16f;
+  constexpr float kBelowTop = FMT == kE4M3 ? 128.0f : 16384.0f;
+  if (nan || lo < kMinSub) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) health_zero4(out[j], h);
+  }
+  if (nan || hi >= kBelowTop) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) health_near4<FMT>(out[j], h);
+  }
 }
 template <int FMT>
 __device__ __forceinline__ void health_code1(uint32_t code, Health& h) {
@@ -127,10 +148,13 @@ __device__ __forceinline__ void health_f32(uint32_t d, Health& h) {
 template <int FMT, bool STATS = false>
 __device__ __forceinline__ u32x4 cast16_bf16(const uint32_t (&d)[8], float s, u16x2& amax2,
                                               uint32_t& sat, bool want_sat, Health* h = nullptr) {
-  u16x2 gm = {0, 0};
+  u16x2 gm = {0, 0}, gn = {0x7FFF, 0x7FFF};
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    gm = __builtin_elementwise_max(gm, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
+  for (int j = 0; j < 8; ++j) {
+    const u16x2 m = __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu);
+    gm = __builtin_elementwise_max(gm, m);
+    if constexpr (STATS) gn = __builtin_elementwise_min(gn, m);
+  }
   amax2 = __builtin_elementwise_max(amax2, gm);
   const bool nan = gm.x > 0x7F80u || gm.y > 0x7F80u;
   u32x4 out;
@@ -143,8 +167,9 @@ __device__ __forceinline__ u32x4 cast16_bf16(const uint32_t (&d)[8], float s, u1
     if (want_sat) sat += sat4<FMT>(a, b, c, e);
   }
   if constexpr (STATS) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) health_codes<FMT>(out[j], *h);
+    const float lo = fabsf(__uint_as_float((uint32_t)min(gn.x, gn.y) << 16) * s);
+    const float hi = fabsf(__uint_as_float((uint32_t)max(gm.x, gm.y) << 16) * s);
+    health_group<FMT>(out, lo, hi, nan, *h);
     if (gm.x >= 0x7F80u || gm.y >= 0x7F80u) {  // some NaN or infinity in the group
 #pragma unroll
       for (int j = 0; j < 8; ++j) health_bf16_pair(d[j], *h);
@@ -156,9 +181,12 @@ __device__ __forceinline__ u32x4 cast16_bf16(const uint32_t (&d)[8], float s, u1
 template <int FMT, bool STATS = false>
 __device__ __forceinline__ u32x4 cast16_f32(const uint32_t (&d)[16], float s, uint32_t& amax,
                                              uint32_t& sat, bool want_sat, Health* h = nullptr) {
-  uint32_t gm = 0;
+  uint32_t gm = 0, gn = 0x7FFFFFFFu;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) gm = max(gm, d[i] & 0x7FFFFFFFu);
+  for (int i = 0; i < 16; ++i) {
+    gm = max(gm, d[i] & 0x7FFFFFFFu);
+    if constexpr (STATS) gn = min(gn, d[i] & 0x7FFFFFFFu);
+  }
   amax = max(amax, gm);
   const bool nan = gm > 0x7F800000u;
   u32x4 out;
@@ -171,8 +199,7 @@ __device__ __forceinline__ u32x4 cast16_f32(const uint32_t (&d)[16], float s, ui
     if (want_sat) sat += sat4<FMT>(v[0], v[1], v[2], v[3]);
   }
   if constexpr (STATS) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) health_codes<FMT>(out[j], *h);
+    health_group<FMT>(out, fabsf(__uint_as_float(gn) * s), fabsf(__uint_as_float(gm) * s), nan, *h);
     if (gm >= 0x7F800000u) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) health_f32(d[i], *h);
@@ -181,24 +208,50 @@ __device__ __forceinline__ u32x4 cast16_f32(const uint32_t (&d)[16], float s, ui
   return out;
 }
 
-// Sums the workgroup's health counts into g[0..3] (NaN, Inf, zero, near-max):
-// wave sums, LDS (4 words per wave from `smem`), one atomic per nonzero count.
-__device__ __forceinline__ void block_commit_health(const Health& h, unsigned long long* g,
-                                                    uint32_t* smem) {
+// Commits a workgroup's amax bits, saturation count and (STATS) health counts
+// (NaN, Inf, zero, near-max into g_health[0..3]): wave reductions, one LDS word
+// per wave and quantity, then wave 0 reduces across the waves in parallel (lane
+// w takes wave w's words) and issues at most one atomic per quantity.  The amax
+// atomic is skipped when the global value already covers the workgroup's: it
+// only grows, and a stale read only costs an extra atomic.
+template <bool STATS>
+__device__ __forceinline__ void block_commit(uint32_t amax_bits, uint32_t sat, const Health& h,
+                                             uint32_t* g_amax, unsigned long long* g_sat,
+                                             unsigned long long* g_health, uint32_t* smem) {
+  constexpr int NQ = STATS ? 6 : 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint32_t v[4] = {h.nan, h.inf, h.zero, h.near};
+  uint32_t v[NQ];
+  v[0] = g_amax ? wave_max_u32(amax_bits) : 0u;
+  v[1] = (g_sat && __any(sat != 0)) ? wave_sum_u32(sat) : 0u;  // most waves saturate nothing
+  if constexpr (STATS) {
+    const uint32_t c[4] = {h.nan, h.inf, h.zero, h.near};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = wave_sum_u32(v[k]);
+    for (int k = 0; k < 4; ++k) v[2 + k] = __any(c[k] != 0) ? wave_sum_u32(c[k]) : 0u;
+  }
   if (lane == 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) smem[k * nw + wave] = v[k];
+    for (int k = 0; k < NQ; ++k) smem[k * nw + wave] = v[k];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k = 0; k < 4; ++k) {
-      uint32_t t = 0;
-      for (int w = 0; w < nw; ++w) t += smem[k * nw + w];
-      if (t) atomicAdd(g + k, (unsigned long long)t);
+  if (wave == 0) {
+    uint32_t t[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) t[k] = lane < nw ? smem[k * nw + lane] : 0u;
+    t[0] = wave_max_u32(t[0]);
+#pragma unroll
+    for (int k = 1; k < NQ; ++k) t[k] = wave_sum_u32(t[k]);
+    if (lane == 0) {
+      if (g_amax) {
+        const uint32_t mb = canonical_amax_bits(t[0]);
+        if (mb > __hip_atomic_load(g_amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+          atomicMax(g_amax, mb);
+      }
+      if (g_sat && t[1]) atomicAdd(g_sat, (unsigned long long)t[1]);
+      if constexpr (STATS) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (t[2 + k]) atomicAdd(g_health + k, (unsigned long long)t[2 + k]);
+      }
     }
   }
 }
@@ -228,7 +281,7 @@ struct CastArgs {
 // new ones start at once.  Atomics on one address serialise (about 11 ns each),
 // so workgroups are large (1024 threads: few resident workgroups all meeting the
 // freshly reset amax at once) and skip the amax atomic when the global value
-// already covers theirs (see block_commit_amax_sat).
+// already covers theirs (see block_commit).
 #ifndef FP8DS_CAST_GROUPS
 #define FP8DS_CAST_GROUPS 4
 #endif
@@ -350,9 +403,8 @@ __global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastAr
       }
     }
   }
-  block_commit_amax_sat(amax, sat, p.amax ? p.amax + b : nullptr, want_sat ? p.sat + b : nullptr,
-                        red);
-  if constexpr (STATS) block_commit_health(h, p.health + 4 * b, red + 2 * (T / 64));
+  block_commit<STATS>(amax, sat, h, p.amax ? p.amax + b : nullptr, want_sat ? p.sat + b : nullptr,
+                      STATS ? p.health + 4 * b : nullptr, red);
 }
 
 // ------------------------------------------------------------------ cast + transposed copy
@@ -495,8 +547,7 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(
       }
     }
   }
-  block_commit_amax_sat(amax, sat, g_amax, g_sat, red);
-  if constexpr (STATS) block_commit_health(h, g_health, red + 8);
+  block_commit<STATS>(amax, sat, h, g_amax, g_sat, g_health, red);
 }
 
 // ------------------------------------------------------------------ host launchers

@@ -83,36 +83,5 @@ __device__ __forceinline__ uint32_t canonical_amax_bits(uint32_t m) {
   return m > 0x7F800000u ? 0x7FC00000u : m;
 }
 
-// Block-wide (blockDim.x threads, multiple of 64) max and sum, then one atomic
-// each into global memory.  `smem` needs 2 * (blockDim.x / 64) words.
-__device__ __forceinline__ void block_commit_amax_sat(uint32_t amax_bits, uint32_t sat,
-                                                      uint32_t* g_amax, unsigned long long* g_sat,
-                                                      uint32_t* smem) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  if (g_amax) amax_bits = wave_max_u32(amax_bits);
-  if (g_sat && __any(sat != 0)) sat = wave_sum_u32(sat);  // most waves saturate nothing
-  if (lane == 0) {
-    smem[wave] = amax_bits;
-    smem[nwaves + wave] = sat;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t m = 0, s = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      m = max(m, smem[w]);
-      s += smem[nwaves + w];
-    }
-    if (g_amax) {
-      // The global value only grows, so a workgroup whose maximum is already
-      // covered can skip the atomic (a stale read only costs an extra atomic).
-      const uint32_t mb = canonical_amax_bits(m);
-      if (mb > __hip_atomic_load(g_amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-        atomicMax(g_amax, mb);
-    }
-    if (g_sat && s) atomicAdd(g_sat, (unsigned long long)s);
-  }
-}
 
 }  // namespace fp8ds

@@ -37,8 +37,14 @@ class DelayedScalingLinear:
     tensor X, W, dY) and its fwd(+bwd) step."""
 
     def __init__(self, hist_len: int = 16, algo: int = ALGO_MAX, margin: int = 0,
-                 fmts=(E4M3, E4M3, E5M2), device="cuda", health: bool = False):
+                 fmts=(E4M3, E4M3, E5M2), device="cuda", health: bool = False,
+                 health_every: int = 1):
         self.health = health
+        # the counting cast costs ~30% more than the plain one on large tensors:
+        # run it on every `health_every`-th step only (the pages check every 100)
+        self.health_every = max(1, int(health_every))
+        self.steps = 0
+        self.health_step = -1  # step whose counts `counts` holds
         self.hist_len = hist_len
         self.algo = algo
         self.margin = margin
@@ -60,7 +66,8 @@ class DelayedScalingLinear:
 
     def _cast(self, t, x, q, q_t, stream):
         s, su, am = self.scale, self.scale_used, self.amax
-        if self.health:
+        if self.health and self.steps % self.health_every == 0:
+            self.health_step = self.steps
             fp8ds_cast_health(x, self.fmts[t], s[t:t + 1], q, self.counts[t], q_t, su[t:t + 1],
                               am[t:t + 1], stream)
         else:
@@ -68,11 +75,14 @@ class DelayedScalingLinear:
                        self.sat[t:t + 1], stream)
 
     def health_report(self):
-        """Host copy of the last step's counts: {"x"|"w"|"dy": {name: count}} (synchronises)."""
-        if self.counts is None:
+        """Host copy of the counts of the last counted step:
+        {"step": i, "x"|"w"|"dy": {name: count}} (synchronises), or None."""
+        if self.counts is None or self.health_step < 0:
             return None
         c = self.counts.cpu().tolist()
-        return {k: dict(zip(HEALTH_NAMES, c[i])) for i, k in enumerate(("x", "w", "dy"))}
+        rep = {k: dict(zip(HEALTH_NAMES, c[i])) for i, k in enumerate(("x", "w", "dy"))}
+        rep["step"] = self.health_step
+        return rep
 
     def _buf(self, name, shape, dtype):
         t = self._bufs.get(name)
@@ -152,6 +162,7 @@ class DelayedScalingLinear:
             n_upd = 3
         fp8ds_scale_update(self.history[:n_upd], self.cursor[:n_upd], am[:n_upd],
                            self.fmts[:n_upd], self.algo, self.margin, s[:n_upd], None, stream)
+        self.steps += 1
         return out
 
 

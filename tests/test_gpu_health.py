@@ -73,3 +73,32 @@ def test_health_counts_are_reset_each_call():
         dsg.fp8ds_cast_health(x, dsg.E4M3, s, q, counts)
     torch.cuda.synchronize()
     assert counts.cpu().numpy().tolist() == [0, 8, 0, 8, 8]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("fmt", [dsg.E4M3, dsg.E5M2])
+@pytest.mark.parametrize("scale", [1.0, -1.5, 2.0**-6])
+def test_health_counts_at_the_group_bounds(dtype, fmt, scale):
+    """Groups of 16 built around the values where the count changes: ties to
+    zero, the smallest subnormal, the binade below the top, values that round
+    into the top binade; negative and small scales included."""
+    top = 256.0 if fmt == dsg.E4M3 else 32768.0
+    sub = 2.0**-9 if fmt == dsg.E4M3 else 2.0**-16
+    edge = np.array([sub / 2, sub, sub * 0.75, sub * 1.25, top / 2, top * 0.97, top * 0.9,
+                     top - 1, top, 0.0, -sub / 2, 1.0, top * 1.75, top / 2 - 1, 3.0, -top],
+                    np.float32)
+    rng = np.random.default_rng(int(abs(scale) * 1e6) + fmt)
+    groups = [np.abs(rng.normal(1.0, 0.1, 16)).astype(np.float32) for _ in range(30)]
+    for i in range(30):
+        groups[i][rng.integers(0, 16)] = edge[i % len(edge)] / np.float32(abs(scale))
+    x32 = np.concatenate(groups)
+    xd, xw = to_dev(x32, dtype)
+    s = torch.tensor([scale], dtype=torch.float32, device=DEV)
+    q = torch.zeros(x32.size, dtype=torch.uint8, device=DEV)
+    counts = torch.zeros(dsg.HEALTH_COUNTS, dtype=torch.int64, device=DEV)
+    dsg.fp8ds_cast_health(xd, fmt, s, q, counts)
+    torch.cuda.synchronize()
+    exp = ohealth.cast_health(xw, np.float32(scale), fmt)
+    assert dict(zip(dsg.HEALTH_NAMES, counts.cpu().numpy().tolist())) == exp
+    codes, _ = ofp8.cast(xw, np.float32(scale), fmt)
+    assert np.array_equal(q.cpu().numpy(), codes)

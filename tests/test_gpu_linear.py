@@ -150,19 +150,27 @@ def test_decoder_projection_health_counts():
 
     M = 512
     lin = DelayedScalingLinear(hist_len=16, algo=dsg.ALGO_MAX, margin=0, health=True)
+    sparse = DelayedScalingLinear(hist_len=16, algo=dsg.ALGO_MAX, margin=0, health=True,
+                                  health_every=4)
     states = oracle_states(16)
     saw_saturation = False
     for step in range(10):
         xb, wb, dyb = workloads.llama_tensors("k_proj", step, m=M)
         out = lin.step(dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb))
+        sparse.step(dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb))
         x, w, dy = obf16.widen(xb), obf16.widen(wb), obf16.widen(dyb)
         ref = olinear.train_step(x, w, dy, states, dsg.ALGO_MAX, 0)
         rep = lin.health_report()
+        srep = sparse.health_report()
+        assert srep["step"] == step - step % 4  # counted every 4th step only
+        if step % 4 == 0:
+            assert {k: srep[k] for k in ("x", "w", "dy")} == {k: rep[k] for k in ("x", "w", "dy")}
         for nm, ck, v in (("x", "cast_x", x), ("w", "cast_w", w), ("dy", "cast_dy", dy)):
             c = ref[ck]
             exp = ohealth.cast_health(v, c.scale_used, states[nm].fmt)
             assert rep[nm] == exp, (step, nm, rep[nm], exp)
             saw_saturation |= exp["saturated"] > 0
+        assert rep["step"] == step
         assert np.array_equal(out["xq"].cpu().numpy(), ref["cast_x"].codes)
         compare_state(lin, states)
     assert saw_saturation  # the 50x batch saturates X's cast
