@@ -31,8 +31,13 @@ Parity status of each function (what pins it, see ``tests/test_oracle_*.py``):
   brute-force triple loop).
 * ``bf16.round_to_bf16``: pinned (torch's fp32->bf16 conversion on fp32
   inputs, exhaustive bf16 round trip, hand-checked ties).
+* ``adamw.*``: pinned (torch.optim.AdamW in float64 over 25 steps, the
+  first-step lr*sign(g) closed form, pure decay under zero gradients, linear
+  motion under a constant gradient, a 50-digit decimal evaluation of one step,
+  the unscale and skip rules).
+* ``health.cast_health``: pinned (hand-worked E4M3 / E5M2 cases).
 * Parity unpinned: nothing in the oracle; on the GPU side the fp32 summation
   order of the accumulator is bounded, not pinned (see ``gemm.py``).
 """
 
-from . import amax, bf16, fp8, gemm, linear, scaling  # noqa: F401
+from . import adamw, amax, bf16, fp8, gemm, health, linear, scaling  # noqa: F401
