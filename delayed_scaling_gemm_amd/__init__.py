@@ -7,7 +7,8 @@ runs in the library's HIP kernels.  There is no fallback: if the library is not
 built or cannot be loaded, every call raises.
 
 Functions keep the C names: ``fp8ds_amax``, ``fp8ds_cast``, ``fp8ds_cast_health``,
-``fp8ds_cast_batched``, ``fp8ds_scale_update``, ``fp8ds_gemm``, ``fp8ds_gemm_batched``.
+``fp8ds_cast_batched``, ``fp8ds_scale_update``, ``fp8ds_gemm``, ``fp8ds_gemm_batched``,
+``fp8ds_adamw``.
 """
 
 from __future__ import annotations
@@ -61,6 +62,10 @@ def _declare(lib):
     lib.fp8ds_gemm.restype = i32
     lib.fp8ds_gemm.argtypes = [i32, i32, i64, i64, i64, vp, i32, i64, vp, vp, i32, i64, vp, vp, i32,
                                i64, vp, i32, vp]
+    f = c.c_float
+    lib.fp8ds_adamw.restype = i32
+    lib.fp8ds_adamw.argtypes = [vp, vp, i32, vp, vp, i64, i64, f, f, f, f, f, f, i64, vp, i32, vp,
+                                vp, vp, vp, vp, vp, vp]
     lib.fp8ds_gemm_batched.restype = i32
     lib.fp8ds_gemm_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i32, i64, i64, vp, vp, i32,
                                        i64, i64, vp, vp, i32, i64, i64, vp, i32, vp]
@@ -289,6 +294,42 @@ def fp8ds_gemm_batched(opa, opb, M, N, K, batch, a, fa, lda, stride_a, scale_a, 
                                     _ptr(scale_a), _ptr(b), fb, ldb, stride_b, _ptr(scale_b),
                                     _ptr(c), _dtype_code(c), ldc, stride_c, _ptr(amax_c), mma,
                                     _stream(stream)))
+
+
+
+def fp8ds_adamw(w, g, m, v, lr, beta1, beta2, eps, weight_decay, step, grad_scale=1.0,
+                grad_amax=None, fmt=E4M3, scale=None, q=None, q_t=None, scale_used=None,
+                amax=None, sat_count=None, stream=None):
+    """Fused AdamW step on the fp32 master weights ``w`` ([rows, cols] or 1-D),
+    moments ``m``, ``v`` (fp32, in place) with gradient ``g`` (bf16 or fp32), step
+    count ``step`` >= 1; with ``scale`` also the FP8 copy of the new weights into
+    ``q`` (uint8; ``q_t`` transposed, ``scale_used``, ``amax``, ``sat_count`` as
+    ``fp8ds_cast``).
+    ``grad_amax`` (fp32 device scalar): a non-finite value skips the update."""
+    import torch
+
+    rows, cols = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, w.numel())
+    n = rows * cols
+    f32 = (torch.float32,)
+    for t, name in ((w, "w"), (m, "m"), (v, "v")):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        _need(t, name, f32, n)
+    if g is None:
+        raise ValueError("g is required")
+    _need(g, "g", (torch.bfloat16, torch.float32), n)
+    _need(grad_amax, "grad_amax", f32, 1)
+    _need(q, "q", (torch.uint8,), n)
+    _need(q_t, "q_t", (torch.uint8,), n)
+    _need(scale, "scale", f32, 1)
+    _need(scale_used, "scale_used", f32, 1)
+    _need(amax, "amax", f32, 1)
+    _need(sat_count, "sat_count", (torch.int64,), 1)
+    _check(lib().fp8ds_adamw(_ptr(w), _ptr(g), _dtype_code(g), _ptr(m), _ptr(v), rows, cols,
+                             float(lr), float(beta1), float(beta2), float(eps),
+                             float(weight_decay), float(grad_scale), int(step), _ptr(grad_amax),
+                             fmt, _ptr(scale), _ptr(q), _ptr(q_t), _ptr(scale_used), _ptr(amax),
+                             _ptr(sat_count), _stream(stream)))
 
 
 def abi_version() -> int:

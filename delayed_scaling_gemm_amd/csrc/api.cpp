@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -73,6 +74,7 @@ const char* fp8ds_status_string(int status) {
     case FP8DS_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
     case FP8DS_ERR_HIP: return "HIP runtime error";
     case FP8DS_ERR_UNSUPPORTED: return "unsupported combination";
+    case FP8DS_ERR_VALUE: return "scalar argument out of range";
     default: return "unknown status";
   }
 }
@@ -270,6 +272,60 @@ int fp8ds_gemm_batched(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t
                        hipStream_t stream) {
   return gemm_common("fp8ds_gemm_batched", opa, opb, M, N, K, batch, A, fa, lda, stride_a, scale_a,
                      B, fb, ldb, stride_b, scale_b, C, ct, ldc, stride_c, amax_c, mma, stream);
+}
+
+int fp8ds_adamw(float* w, const void* g, fp8ds_dtype gt, float* m, float* v, int64_t rows,
+                int64_t cols, float lr, float beta1, float beta2, float eps, float weight_decay,
+                float grad_scale, int64_t step, const float* grad_amax, fp8ds_format fmt,
+                const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
+                uint64_t* sat_count, hipStream_t stream) {
+#pragma clang fp contract(off)
+  const char* who = "fp8ds_adamw";
+  if (!valid_dtype(gt)) return fail(FP8DS_ERR_ENUM, "%s: bad gradient dtype %d", who, (int)gt);
+  if (rows < 0 || cols < 0 || (cols > 0 && rows > kMaxElems / cols))
+    return fail(FP8DS_ERR_SHAPE, "%s: bad shape %lld x %lld", who, (long long)rows,
+                (long long)cols);
+  if (!(std::isfinite(lr) && std::isfinite(weight_decay) && beta1 >= 0.0f && beta1 < 1.0f &&
+        beta2 >= 0.0f && beta2 < 1.0f && std::isfinite(eps) && eps > 0.0f &&
+        std::isfinite(grad_scale) && grad_scale > 0.0f && step >= 1))
+    return fail(FP8DS_ERR_VALUE,
+                "%s: need finite lr and weight_decay, 0 <= beta1, beta2 < 1, finite eps > 0, "
+                "finite grad_scale > 0 and step >= 1",
+                who);
+  // the FP8 copy is requested by a scale
+  const bool cast = scale != nullptr;
+  if (cast && !valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "%s: bad format %d", who, (int)fmt);
+  if (!cast && (q || q_t || scale_used || amax || sat_count))
+    return fail(FP8DS_ERR_NULL, "%s: q, q_t, scale_used, amax and sat_count need scale", who);
+  const int64_t n = rows * cols;
+  if (n > 0) {
+    if (!w || !g || !m || !v) return fail(FP8DS_ERR_NULL, "%s: w, g, m and v are required", who);
+    if (cast && !q) return fail(FP8DS_ERR_NULL, "%s: q is null", who);
+    if (!aligned16(w) || !aligned16(g) || !aligned16(m) || !aligned16(v) || (q && !aligned16(q)) ||
+        (q_t && !aligned16(q_t)))
+      return fail(FP8DS_ERR_ALIGN, "%s: w, g, m, v, q and q_t must be 16-byte aligned", who);
+  }
+  if (q_t && (rows + 127) / 128 > 65535)
+    return fail(FP8DS_ERR_SHAPE, "%s: a transposed copy supports at most %d rows", who,
+                65535 * 128);
+  // Per-step constants: float64 from the fp32 hyperparameters, one rounding to fp32.
+  const double lr_d = lr, wd_d = weight_decay, b1 = beta1, b2 = beta2;
+  fp8ds::AdamWConsts c;
+  c.b1 = beta1;
+  c.b2 = beta2;
+  c.omb1 = (float)(1.0 - b1);
+  c.omb2 = (float)(1.0 - b2);
+  c.eps = eps;
+  c.decay = (float)(1.0 - lr_d * wd_d);
+  c.step_size = (float)(lr_d / (1.0 - std::pow(b1, (double)step)));
+  c.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, (double)step)));
+  c.grad_scale = grad_scale;
+  fp8ds::AdamWLaunch a{w, g, gt == FP8DS_BF16, m, v, rows, cols, c, grad_amax, (int)fmt, scale,
+                       cast ? q : nullptr, cast ? q_t : nullptr, amax, sat_count};
+  hipError_t e = hipSuccess;
+  if (cast) e = fp8ds::launch_prologue(1, scale, scale_used, amax, sat_count, stream);
+  if (e == hipSuccess && n > 0) e = fp8ds::launch_adamw(a, stream);
+  return hip_status(e, who);
 }
 
 }  // extern "C"

@@ -25,6 +25,34 @@ hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t
                                  const float* scale, uint8_t* q, uint8_t* qt, float* amax,
                                  uint64_t* sat, uint64_t* health, hipStream_t stream);
 
+// Fused AdamW step + FP8 cast of the updated weights.  The per-step fp32
+// constants are derived on the host from the hyperparameters and the step count.
+struct AdamWConsts {
+  float b1, b2, omb1, omb2;  // beta1, beta2, 1 - beta1, 1 - beta2
+  float eps;
+  float decay;         // 1 - lr * weight_decay
+  float step_size;     // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+  float grad_scale;
+};
+struct AdamWLaunch {
+  float* w;          // [rows x cols] fp32 master weights, updated in place
+  const void* g;     // gradient, BF16 (g_bf16) or fp32
+  bool g_bf16;
+  float* m;          // first moment, fp32, in place
+  float* v;          // second moment, fp32, in place
+  int64_t rows, cols;
+  AdamWConsts c;
+  const float* grad_amax;  // or null: a non-finite value skips the update
+  int fmt;
+  const float* scale;      // delayed scale of the weights (q != null)
+  uint8_t* q;              // or null: no cast
+  uint8_t* qt;             // or null: no transposed copy (requires q)
+  float* amax;             // or null; reset by launch_prologue
+  uint64_t* sat;           // or null; reset by launch_prologue
+};
+hipError_t launch_adamw(const AdamWLaunch& a, hipStream_t stream);
+
 // History push + window reduction + next scale for n tensors.
 // fmt_bits: bit t set = tensor t is E5M2.
 struct FmtBits {

@@ -10,6 +10,7 @@
  *   ->  dequant by 1/(s_a * s_b) into BF16, with the output amax fused.
  *
  * Sources (cited by page title and section):
+ *   [P1] "算子与编译器：FP8 训练与优化器 Kernel" (charles2530.github.io)
  *   [P2] "FP8 混合精度训练工程实践：从 H100 到大模型训练的范式跃迁" (ybb.press)
  *   [P3] "LLM FP8 微调上线生产实战：用 Amax Scaling、层级白名单与 BF16 回退守住收敛"
  *        (oh-bug.com)
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FP8DS_ABI_VERSION 3
+#define FP8DS_ABI_VERSION 4
 
 typedef enum {
   FP8DS_OK = 0,
@@ -54,7 +55,8 @@ typedef enum {
   FP8DS_ERR_ENUM = -3,        /* a format, dtype, op or algo value out of range */
   FP8DS_ERR_ALIGN = -4,       /* pointer or leading dimension not 16-byte aligned */
   FP8DS_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
-  FP8DS_ERR_UNSUPPORTED = -6  /* valid but unsupported combination (e.g. TT) */
+  FP8DS_ERR_UNSUPPORTED = -6, /* valid but unsupported combination (e.g. TT) */
+  FP8DS_ERR_VALUE = -7        /* a scalar argument out of its range (fp8ds_adamw) */
 } fp8ds_status;
 
 /* FP8 formats ([P2] §一 "FP8 格式设计"; [P3] §核心原理 "E4M3 与 E5M2 承担不同职责"):
@@ -250,6 +252,60 @@ int fp8ds_gemm_batched(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t
                        int64_t stride_b, const float* scale_b, void* C, fp8ds_dtype ct,
                        int64_t ldc, int64_t stride_c, float* amax_c, fp8ds_mma mma,
                        hipStream_t stream);
+
+/*
+ * fp8ds_adamw -- fused AdamW step on FP32 master weights that also writes the
+ * FP8 copy of the updated weights for the next forward.
+ * "算子与编译器：FP8 训练与优化器 Kernel" (charles2530.github.io): §"FP8 训练主路径图"
+ * (unscale/clip -> fused optimizer -> master weight -> cast/scale to FP8) and
+ * §"Fused Optimizer 的意义" (one kernel reads the gradient, updates both moments,
+ * applies the bias corrections and the weight decay, updates the parameter);
+ * [P2] §"自动混合精度与 FP8 的协同" (gradient un-scaling, FP32 AdamW, the updated
+ * weights cast to FP8 with scaling for the next forward).
+ *
+ * The pages name AdamW without its formula; this is AdamW with decoupled weight
+ * decay (Loshchilov & Hutter) and bias-corrected moments (Kingma & Ba).  Per
+ * element, each operation one correctly rounded fp32 operation in this order,
+ * no fused multiply-add:
+ *   g' = g * grad_scale
+ *   m  = beta1 * m + (1 - beta1) * g'
+ *   v  = beta2 * v + ((1 - beta2) * g') * g'
+ *   w  = decay * w - step_size * (m / (sqrt(v) * inv_sqrt_bc2 + eps))
+ * with the fp32 constants decay = 1 - lr*weight_decay, 1 - beta1, 1 - beta2,
+ * step_size = lr / (1 - beta1^step), inv_sqrt_bc2 = 1 / sqrt(1 - beta2^step),
+ * each evaluated in float64 (C library pow and sqrt) and rounded once.
+ * If scale != NULL, the updated weights are then cast exactly as fp8ds_cast
+ * casts them (q, q_t, scale_used, amax, sat_count with fp8ds_cast's meaning, amax
+ * and saturation of the NEW weights), so the next forward needs no weight cast.
+ *
+ *   w          device [rows x cols] fp32 master weights, row-major, updated in place.
+ *   g          device [rows x cols] gradient of dtype gt (BF16 or FP32), read only.
+ *   m, v       device [rows x cols] fp32 first and second moments, updated in
+ *              place (zeros before the first step).  w, g, m, v must not overlap.
+ *   rows,cols  >= 0.  All of w, g, m, v, q, q_t 16-byte aligned.
+ *   lr, weight_decay  finite.   beta1, beta2  in [0, 1).   eps  finite, > 0.
+ *   grad_scale finite, > 0: multiplies the gradient first (1/K for a loss
+ *              scaled by K, times any clipping factor the caller computed).
+ *   step       the step count t >= 1 of this update (bias corrections).
+ *   grad_amax  device or NULL: if it holds an infinity or NaN (e.g. the amax_c of
+ *              the fp8ds_gemm that produced g), the update is skipped -- w, m, v
+ *              are left unchanged -- and the FP8 copy is made of the unchanged w.
+ *   scale      device or NULL: the delayed scale of the weights.  NULL = no FP8
+ *              copy (then q, q_t, scale_used, amax and sat_count must be NULL).
+ *   fmt        FP8 format of the copy (checked when scale != NULL).
+ *   q          device, rows*cols bytes (required with scale when rows*cols > 0): the
+ *              FP8 copy of the new weights.
+ *   q_t        device or NULL: the transposed copy [cols x rows]; rows at most
+ *              65535 * 128.
+ *   scale_used, amax, sat_count  device or NULL: as fp8ds_cast (written also when
+ *              rows*cols == 0).
+ * Out-of-range scalars return FP8DS_ERR_VALUE.
+ */
+int fp8ds_adamw(float* w, const void* g, fp8ds_dtype gt, float* m, float* v, int64_t rows,
+                int64_t cols, float lr, float beta1, float beta2, float eps, float weight_decay,
+                float grad_scale, int64_t step, const float* grad_amax, fp8ds_format fmt,
+                const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
+                uint64_t* sat_count, hipStream_t stream);
 
 #ifdef __cplusplus
 }

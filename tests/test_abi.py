@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8ds_amax", "fp8ds_cast", "fp8ds_cast_batched", "fp8ds_scale_update",
               "fp8ds_gemm", "fp8ds_gemm_batched", "fp8ds_status_string", "fp8ds_last_error",
-              "fp8ds_abi_version"):
+              "fp8ds_abi_version", "fp8ds_adamw", "fp8ds_cast_health"):
         assert n in names
 
 
@@ -35,12 +35,12 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(dsg.LIB_PATH)
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert dsg.abi_version() == 3
+    assert dsg.abi_version() == 4
 
 
 def test_status_strings():
     L = dsg.lib()
-    for s in (0, -1, -2, -3, -4, -5, -6):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.fp8ds_status_string(s)
     assert L.fp8ds_status_string(-99) == b"unknown status"
 
@@ -92,3 +92,32 @@ def test_validation_errors_without_gpu():
     assert L.fp8ds_gemm(0, 1, big, big, 16, p, 0, 16, p, p, 0, 16, p, p, 1, big, None, 0,
                         None) == -2
     assert args
+
+
+def test_adamw_validation_errors_without_gpu():
+    L = dsg.lib()
+    p = 0x1000
+    hp = dict(lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.01, gs=1.0, step=1)
+
+    def call(w=p, g=p, gt=1, m=p, v=p, rows=4, cols=16, grad_amax=None, fmt=0, scale=p, q=p,
+             q_t=None, scale_used=None, amax=None, sat=None, **kw):
+        h = dict(hp, **kw)
+        st = L.fp8ds_adamw(w, g, gt, m, v, rows, cols, h["lr"], h["b1"], h["b2"], h["eps"],
+                           h["wd"], h["gs"], h["step"], grad_amax, fmt, scale, q, q_t, scale_used,
+                           amax, sat, None)
+        return st, L.fp8ds_last_error().decode()
+
+    assert call(gt=5)[0] == -3
+    assert call(fmt=7)[0] == -3
+    assert call(rows=-1)[0] == -2
+    for bad in (dict(b1=1.0), dict(b2=-0.1), dict(eps=0.0), dict(gs=0.0), dict(step=0),
+                dict(lr=float("inf")), dict(wd=float("nan")), dict(eps=float("inf"))):
+        st, msg = call(**bad)
+        assert st == -7 and "fp8ds_adamw" in msg, bad
+    assert call(q=None, q_t=p)[0] == -1        # a scale asks for q
+    assert call(scale=None)[0] == -1           # q without a scale
+    assert call(scale=None, q=None, amax=p)[0] == -1
+    assert call(m=None)[0] == -1
+    assert call(g=p + 4)[0] == -4
+    assert call(q_t=p + 8)[0] == -4
+    assert call(rows=65535 * 128 + 1, cols=1, q_t=p)[0] == -2

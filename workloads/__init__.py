@@ -207,3 +207,19 @@ def small_batch(batch: int = 512, m: int = 256, k: int = 256, n: int = 256, step
     x = normal(batch * m * k, seed_of(cfg, step, 100 + TID_X))
     w = normal(batch * k * n, seed_of(cfg, 0, 100 + TID_W), 0.02)
     return (to_bf16_bits(x).reshape(batch, m, k), to_bf16_bits(w).reshape(batch, k, n))
+
+
+TID_M, TID_V, TID_G = 4, 5, 6
+
+
+def adamw_state(rows: int, cols: int, step: int = 0):
+    """Optimizer state of a [rows, cols] weight: fp32 master W ~ N(0, 0.02^2),
+    first moment ~ N(0, 1e-3^2), second moment ~ U(0, 1e-4) (the size of squared
+    gradients of about 1e-2), and a heavy-tailed bf16 gradient (dW)."""
+    cfg = 6
+    n = rows * cols
+    w = normal(n, seed_of(cfg, 0, TID_W), 0.02).reshape(rows, cols)
+    m = normal(n, seed_of(cfg, 0, TID_M), 1e-3).reshape(rows, cols)
+    v = uniform(n, seed_of(cfg, 0, TID_V), 0.0, 1e-4).reshape(rows, cols)
+    g = heavy_tail_grad(n, seed_of(cfg, step, TID_G))
+    return w, m, v, to_bf16_bits(g).reshape(rows, cols)
