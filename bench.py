@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-stress", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration throughput report")
+    ap.add_argument("--no-optimizer", action="store_true",
+                    help="skip the fused AdamW + weight-cast measurement")
     ap.add_argument("--no-fp8-path", action="store_true",
                     help="skip the context timing of the FP8-MFMA datapath")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -182,6 +184,56 @@ def stress_cast(torch, dsg, workloads, dev, iters=10):
     out["amax"] = {"ms": round(ms, 4), "GB/s": round(2.0 * n / (ms * 1e-3) / 1e9, 1),
                    "frac_hbm": round(2.0 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     del x, q
+    torch.cuda.empty_cache()
+    return out
+
+
+def optimizer_report(torch, dsg, workloads, dev, rows=4096, cols=4096, iters=10):
+    """The fused AdamW step on the benchmarked Linear's [4096 x 4096] fp32 master
+    weights with its BF16 dW, writing Wq and Wq^T for the next forward (28
+    algorithmic bytes per element: read w, m, v, g = 14; write w, m, v, q, q_t =
+    14), against the unfused pair: the update alone (26 B) and the transposing
+    cast of the fp32 weights (6 B)."""
+    print("[bench] fused AdamW 4096x4096", file=sys.stderr, flush=True)
+    w, m, v, gbits = workloads.adamw_state(rows, cols)
+    n = rows * cols
+    wd, md, vd = (torch.from_numpy(a).to(dev) for a in (w, m, v))
+    g = torch.from_numpy(gbits.view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    qt = torch.empty(n, dtype=torch.uint8, device=dev)
+    s = torch.tensor([448.0 / 0.1], device=dev)
+    su = torch.zeros(1, device=dev)
+    am = torch.zeros(1, device=dev)
+    sat = torch.zeros(1, dtype=torch.int64, device=dev)
+    ga = torch.tensor([float(np.abs((gbits.astype(np.uint32) << 16).view(np.float32)).max())],
+                      device=dev)
+    stream = torch.cuda.current_stream()
+    hp = (1e-4, 0.9, 0.999, 1e-8, 0.01)
+
+    def fused():
+        dsg.fp8ds_adamw(wd, g, md, vd, *hp, 10, grad_amax=ga, fmt=dsg.E4M3, scale=s, q=q, q_t=qt,
+                        scale_used=su, amax=am, sat_count=sat)
+
+    def update_only():
+        dsg.fp8ds_adamw(wd, g, md, vd, *hp, 10, grad_amax=ga)
+
+    def cast_w():
+        dsg.fp8ds_cast(wd, dsg.E4M3, s, q, qt, su, am, sat)
+
+    out = {"shape": [rows, cols], "grad": "bf16", "fmt": "e4m3"}
+    t = {}
+    for name, fn in (("fused", fused), ("update_only", update_only), ("cast_w_t_fp32", cast_w)):
+        fn()
+        t[name] = time_launches(torch, stream, fn, iters)
+    alg = {"fused": 28.0, "update_only": 26.0, "cast_w_t_fp32": 6.0}
+    for name, ms in t.items():
+        gbps = alg[name] * n / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                     "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+    unfused = t["update_only"] + t["cast_w_t_fp32"]
+    out["unfused_ms"] = round(unfused, 4)
+    out["fused_speedup"] = round(unfused / t["fused"], 3)
+    del wd, md, vd, g, q, qt
     torch.cuda.empty_cache()
     return out
 
@@ -429,6 +481,8 @@ def main():
 
     if not args.no_stress:
         result["cast_stress"] = stress_cast(torch, dsg, workloads, dev)
+    if not args.no_optimizer:
+        result["optimizer"] = optimizer_report(torch, dsg, workloads, dev)
     if not args.no_configs:
         del sets, base
         torch.cuda.empty_cache()

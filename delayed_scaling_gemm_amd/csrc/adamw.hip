@@ -20,9 +20,12 @@
 // Design for gfx950: HBM-bound, 28 bytes per element with a BF16 gradient
 // (read w, m, v 4 B each and g 2 B; write w, m, v and q, q_t 1 B each).  The
 // FP8 copy costs 2 bytes per element here against 6 for a separate cast pass
-// over the weights (read 4, write 2).  Each thread updates 16-element pieces
-// with 16-byte non-temporal loads and stores; the transposed copy goes through
-// the same LDS tile and transposing reads as the standalone cast.
+// over the weights (read 4, write 2).  Each lane updates quads of 4 elements,
+// placed so that every 16-byte non-temporal load and store instruction of a wave
+// covers contiguous runs (lanes owning 64 contiguous bytes each, as the
+// standalone casts' loads do, left every store writing 64 partial lines and
+// measured 1.5 TB/s); the transposed copy goes through the same LDS tile and
+// transposing reads as the standalone cast.
 
 #include <math.h>
 
@@ -50,49 +53,44 @@ __device__ __forceinline__ bool adamw_skip(const AdamWLaunch& p) {
   return b >= 0x7F800000u;  // infinity or NaN
 }
 
-// Updates the 16 elements at `off` (16-byte aligned in every array) and returns
-// the new weights' bits in wb.  Skipped steps only read w.
+// Updates four quads of 4 consecutive elements, quad k at element offset
+// off[k] (16-byte aligned in the fp32 arrays, 8-byte in a BF16 gradient), and
+// returns the new weights' bits in wb (quad k in wb[4k .. 4k+3]).  Callers
+// place the quads of consecutive lanes next to each other, so every load and
+// store instruction of a wave covers one contiguous run (1 KB of fp32).
+// Skipped steps only read w.
 template <bool GBF16>
-__device__ __forceinline__ void adamw16(const AdamWLaunch& p, int64_t off, bool skip,
-                                        uint32_t (&wb)[16]) {
-  u32x4* wp = reinterpret_cast<u32x4*>(p.w + off);
+__device__ __forceinline__ void adamw_quads(const AdamWLaunch& p, const int64_t (&off)[4],
+                                            bool skip, uint32_t (&wb)[16]) {
   u32x4 wv[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) wv[k] = __builtin_nontemporal_load(wp + k);
+  for (int k = 0; k < 4; ++k)
+    wv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.w + off[k]));
   if (skip) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) wb[i] = wv[i >> 2][i & 3];
     return;
   }
-  u32x4* mp = reinterpret_cast<u32x4*>(p.m + off);
-  u32x4* vp = reinterpret_cast<u32x4*>(p.v + off);
-  u32x4 mv[4], vv[4], gv[GBF16 ? 2 : 4];
+  u32x4 mv[4], vv[4], gv[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    mv[k] = __builtin_nontemporal_load(mp + k);
-    vv[k] = __builtin_nontemporal_load(vp + k);
-  }
-  if constexpr (GBF16) {
-    const u32x4* gp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.g) + off);
-    gv[0] = __builtin_nontemporal_load(gp);
-    gv[1] = __builtin_nontemporal_load(gp + 1);
-  } else {
-    const u32x4* gp = reinterpret_cast<const u32x4*>(static_cast<const float*>(p.g) + off);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) gv[k] = __builtin_nontemporal_load(gp + k);
+    mv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.m + off[k]));
+    vv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.v + off[k]));
+    if constexpr (GBF16) {
+      const u32x2 h = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.g) + off[k]));
+      gv[k] = u32x4{h.x << 16, h.x & 0xFFFF0000u, h.y << 16, h.y & 0xFFFF0000u};
+    } else {
+      gv[k] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(static_cast<const float*>(p.g) + off[k]));
+    }
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float g;
-    if constexpr (GBF16) {
-      const uint32_t pair = gv[i >> 3][(i >> 1) & 3];
-      g = __uint_as_float((i & 1) ? (pair & 0xFFFF0000u) : (pair << 16));
-    } else {
-      g = __uint_as_float(gv[i >> 2][i & 3]);
-    }
     float m = __uint_as_float(mv[i >> 2][i & 3]);
     float v = __uint_as_float(vv[i >> 2][i & 3]);
-    const float w = adamw_elem(__uint_as_float(wv[i >> 2][i & 3]), g, m, v, p.c);
+    const float w = adamw_elem(__uint_as_float(wv[i >> 2][i & 3]),
+                               __uint_as_float(gv[i >> 2][i & 3]), m, v, p.c);
     wb[i] = __float_as_uint(w);
     wv[i >> 2][i & 3] = wb[i];
     mv[i >> 2][i & 3] = __float_as_uint(m);
@@ -100,9 +98,9 @@ __device__ __forceinline__ void adamw16(const AdamWLaunch& p, int64_t off, bool 
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    __builtin_nontemporal_store(wv[k], wp + k);
-    __builtin_nontemporal_store(mv[k], mp + k);
-    __builtin_nontemporal_store(vv[k], vp + k);
+    __builtin_nontemporal_store(wv[k], reinterpret_cast<u32x4*>(p.w + off[k]));
+    __builtin_nontemporal_store(mv[k], reinterpret_cast<u32x4*>(p.m + off[k]));
+    __builtin_nontemporal_store(vv[k], reinterpret_cast<u32x4*>(p.v + off[k]));
   }
 }
 
@@ -130,9 +128,10 @@ __device__ __forceinline__ uint32_t cast1(float w, float s, uint32_t& amax, uint
   return encode_fp8<FMT>(y);
 }
 
-// Flat kernel: the rows*cols elements as one array, a 16-element piece per
-// thread (the last piece, if shorter, element by element).  CAST = false is
-// the plain fused AdamW step.
+// Flat kernel: the rows*cols elements as one array.  A workgroup of 256
+// threads owns 4096 consecutive elements; thread t takes the quads at
+// 4t + 1024k, k = 0..3.  The last, partial workgroup goes element by element.
+// CAST = false is the plain fused AdamW step.
 template <bool GBF16, int FMT, bool CAST>
 __global__ __launch_bounds__(256) void adamw_kernel(AdamWLaunch p) {
   __shared__ uint32_t red[2 * 4];
@@ -140,20 +139,27 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamWLaunch p) {
   const bool skip = adamw_skip(p);
   if (!CAST && skip) return;
   const float s = CAST ? p.scale[0] : 1.0f;
-  const int64_t off = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+  const int64_t base = (int64_t)blockIdx.x * 4096 + 4 * threadIdx.x;
   uint32_t amax = 0, sat = 0;
-  if (off + 16 <= n) {
+  if ((int64_t)(blockIdx.x + 1) * 4096 <= n) {
+    const int64_t off[4] = {base, base + 1024, base + 2048, base + 3072};
     uint32_t wb[16];
-    adamw16<GBF16>(p, off, skip, wb);
+    adamw_quads<GBF16>(p, off, skip, wb);
     if constexpr (CAST) {
       const u32x4 codes = cast16_f32<FMT, false>(wb, s, amax, sat, p.sat != nullptr);
-      __builtin_nontemporal_store(codes, reinterpret_cast<u32x4*>(p.q + off));
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        __builtin_nontemporal_store(codes[k], reinterpret_cast<uint32_t*>(p.q + off[k]));
     }
-  } else if (off < n) {
-    for (int64_t i = off; i < n; ++i) {
-      const float w = adamw1<GBF16>(p, i, skip);
-      if constexpr (CAST) p.q[i] = (uint8_t)cast1<FMT>(w, s, amax, sat);
-    }
+  } else {
+    for (int k = 0; k < 4; ++k)
+      for (int j = 0; j < 4; ++j) {
+        const int64_t i = base + 1024 * k + j;
+        if (i < n) {
+          const float w = adamw1<GBF16>(p, i, skip);
+          if constexpr (CAST) p.q[i] = (uint8_t)cast1<FMT>(w, s, amax, sat);
+        }
+      }
   }
   if constexpr (CAST) {
     Health h;
@@ -177,16 +183,27 @@ __global__ __launch_bounds__(256) void adamw_transpose_kernel(AdamWLaunch p) {
   uint32_t amax = 0, sat = 0;
   const bool vec = (r0 + T <= rows) && (c0 + T <= cols) && (cols % 16 == 0) && (rows % 16 == 0);
   if (vec) {
+    // pass i: quad u = 1024 i + 256 k + tid of the tile's 4096 (32 per row), so a
+    // wave instruction covers two 512-byte row runs of fp32
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int piece = tid + 256 * i;
-      const int r = piece >> 3, cp = (piece & 7) * 16;
-      const int64_t off = (r0 + r) * cols + c0 + cp;
+      int64_t off[4];
+      int rr[4], cc[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int u = 1024 * i + 256 * k + tid;
+        rr[k] = u >> 5;
+        cc[k] = (u & 31) * 4;
+        off[k] = (r0 + rr[k]) * cols + c0 + cc[k];
+      }
       uint32_t wb[16];
-      adamw16<GBF16>(p, off, skip, wb);
+      adamw_quads<GBF16>(p, off, skip, wb);
       const u32x4 codes = cast16_f32<FMT, false>(wb, s, amax, sat, p.sat != nullptr);
-      __builtin_nontemporal_store(codes, reinterpret_cast<u32x4*>(p.q + off));
-      tile_park16(tile, r, cp, codes);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        __builtin_nontemporal_store(codes[k], reinterpret_cast<uint32_t*>(p.q + off[k]));
+        tile_park4(tile, rr[k], cc[k], codes[k]);
+      }
     }
     __syncthreads();
     tile_store_qt<4>(tile, p.qt, rows, r0, c0, tid);

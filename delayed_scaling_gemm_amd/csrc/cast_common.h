@@ -286,4 +286,10 @@ __device__ __forceinline__ void tile_park16(uint8_t* tile, int r, int cp, const 
   *reinterpret_cast<u32x2*>(tile + r * T + (((c8 + 1) ^ sw) << 3)) = u32x2{codes.z, codes.w};
 }
 
+// Parks the 4 codes of row r, columns c .. c + 3 (c % 4 == 0) in the same layout.
+__device__ __forceinline__ void tile_park4(uint8_t* tile, int r, int c, uint32_t codes) {
+  constexpr int T = 128;
+  *reinterpret_cast<uint32_t*>(tile + r * T + ((((c >> 3) ^ (r & 7))) << 3) + (c & 4)) = codes;
+}
+
 }  // namespace fp8ds

@@ -8,6 +8,9 @@ Host-side orchestration only (every arithmetic step runs in the HIP library):
         dX = dYq . Wq^T      (NT)             -> BF16 dX
         dW = Xq^T . dYq      (TN)             -> BF16 dW
   end:  one scale update over the X, W, dY histories -> scales of the next step
+  opt:  (optional) adamw_step: fused AdamW on the fp32 master weights with this
+        step's dW, writing Wq, Wq^T, amax_W and the W scale snapshot of the next
+        step, whose forward then skips the W cast
 
 This is the HYBRID recipe ("LLM FP8 微调上线生产实战" §核心原理: E4M3 for forward
 tensors, E5M2 for gradients) with delayed scaling: each cast uses the scale that
@@ -26,8 +29,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (ALGO_MAX, E4M3, E5M2, HEALTH_COUNTS, HEALTH_NAMES, OP_N, OP_T, fp8ds_cast,
-               fp8ds_cast_health, fp8ds_gemm, fp8ds_scale_update)
+from . import (ALGO_MAX, E4M3, E5M2, HEALTH_COUNTS, HEALTH_NAMES, OP_N, OP_T, fp8ds_adamw,
+               fp8ds_cast, fp8ds_cast_health, fp8ds_gemm, fp8ds_scale_update)
 
 X, W, DY = 0, 1, 2
 
@@ -58,6 +61,9 @@ class DelayedScalingLinear:
         self.amax = torch.zeros(3, **f32)
         self.sat = torch.zeros(3, dtype=torch.int64, device=self.device)
         self.amax_y = torch.zeros(1, **f32)
+        self.amax_dw = torch.zeros(1, **f32)  # fused output amax of dW (skip rule)
+        self._w_prepared = None  # master weights whose FP8 copy adamw_step wrote
+        self.w_counts_valid = True
         # health=True: each cast also counts saturated, NaN, Inf, zero and
         # top-binade values (fp8ds_cast_health) into counts[X | W | DY]
         self.counts = (torch.zeros(3, HEALTH_COUNTS, dtype=torch.int64, device=self.device)
@@ -81,6 +87,8 @@ class DelayedScalingLinear:
             return None
         c = self.counts.cpu().tolist()
         rep = {k: dict(zip(HEALTH_NAMES, c[i])) for i, k in enumerate(("x", "w", "dy"))}
+        if not self.w_counts_valid:
+            rep["w"] = None  # the weights' cast was fused into adamw_step: not counted
         rep["step"] = self.health_step
         return rep
 
@@ -140,7 +148,15 @@ class DelayedScalingLinear:
         y = self._buf("y", (M, N), torch.bfloat16)
         s, su, am = self.scale, self.scale_used, self.amax
         self._cast(X, x, xq, None, stream)
-        self._cast(W, w, wq, wqt, stream)
+        if self._w_prepared is not None and self._w_prepared is w:
+            # adamw_step already wrote Wq, Wq^T, amax_W and the W snapshot
+            if self.health and self.steps % self.health_every == 0:
+                self.w_counts_valid = False
+        else:
+            if self.health and self.steps % self.health_every == 0:
+                self.w_counts_valid = True
+            self._cast(W, w, wq, wqt, stream)
+        self._w_prepared = None
         # Y[M, N] = Xq[M, K] . Wq[K, N], with Wq^T stored [N, K] -> op T
         fp8ds_gemm(OP_N, OP_T, M, N, K, xq, self.fmts[X], K, su[X:X + 1], wqt, self.fmts[W], K,
                    su[W:W + 1], y, N, self.amax_y, stream)
@@ -157,13 +173,40 @@ class DelayedScalingLinear:
                        N, su[W:W + 1], dx, K, None, stream)
             # dW[K, N] = Xq^T . dYq         (Xq stored [M, K] = [K' x M'] -> op T)
             fp8ds_gemm(OP_T, OP_N, K, N, M, xq, self.fmts[X], K, su[X:X + 1], dyq, self.fmts[DY],
-                       N, su[DY:DY + 1], dw, N, None, stream)
+                       N, su[DY:DY + 1], dw, N, self.amax_dw, stream)
             out.update(dyq=dyq, dx=dx, dw=dw)
             n_upd = 3
         fp8ds_scale_update(self.history[:n_upd], self.cursor[:n_upd], am[:n_upd],
                            self.fmts[:n_upd], self.algo, self.margin, s[:n_upd], None, stream)
         self.steps += 1
         return out
+
+    def adamw_step(self, w, m, v, lr, step, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                   grad_scale=1.0, stream=None):
+        """Fused AdamW on the fp32 master weights ``w`` [in, out] and moments ``m``,
+        ``v`` with the dW of the last :meth:`step` (step count ``step`` >= 1).
+
+        The same kernel casts the new weights with the W scale the last step's
+        scale update produced, into the Wq / Wq^T buffers, and records their amax:
+        the next :meth:`step` given this ``w`` skips its W cast ("算子与编译器：
+        FP8 训练与优化器 Kernel" §FP8 训练主路径图: fused optimizer -> master weight ->
+        cast to FP8).  The result is bit-identical to updating ``w`` and casting it
+        at the start of the next step.  A non-finite dW amax skips the update
+        (weights and moments stay; their FP8 copy is still made)."""
+        dw = self._bufs.get("dw")
+        if dw is None or tuple(dw.shape) != tuple(w.shape):
+            raise RuntimeError("adamw_step needs the dW of a preceding fwd+bwd step of this shape")
+        if w.dtype != torch.float32:
+            raise TypeError("the master weights must be fp32")
+        K, N = w.shape
+        wq = self._buf("wq", (K, N), torch.uint8)
+        wqt = self._buf("wqt", (N, K), torch.uint8)
+        s, su, am = self.scale, self.scale_used, self.amax
+        fp8ds_adamw(w, dw, m, v, lr, beta1, beta2, eps, weight_decay, step, grad_scale=grad_scale,
+                    grad_amax=self.amax_dw, fmt=self.fmts[W], scale=s[W:W + 1], q=wq, q_t=wqt,
+                    scale_used=su[W:W + 1], amax=am[W:W + 1], sat_count=self.sat[W:W + 1],
+                    stream=stream)
+        self._w_prepared = w
 
 
 class BatchedDelayedScalingLinear:

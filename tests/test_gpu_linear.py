@@ -217,3 +217,62 @@ def test_checkpoint_resume_is_bit_identical(tmp_path):
         for k in ("scale", "amax", "history", "cursor"):
             assert torch.equal(getattr(resumed, k), rs[k]), (step, k)
     assert not torch.equal(scale_only.scale, outs[9][1]["scale"])
+
+
+def test_fused_adamw_step_matches_the_unfused_loop():
+    """Six training steps of the k_proj Linear with fp32 master weights, once with
+    the AdamW update followed by the next step's W cast (unfused), once with
+    adamw_step (update and W cast in one kernel, the next forward skipping its
+    W cast).  Every FP8 operand, every output, the weights, the moments and the
+    scaling state agree bit for bit; at step 3 a NaN in dY makes dW non-finite
+    and both runs skip the update."""
+    M, NAN_STEP = 256, 3
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    _, wb, _ = workloads.llama_tensors("k_proj", 0, m=M)
+    w0 = torch.from_numpy((wb.astype(np.uint32) << 16).view(np.float32)).to(DEV)
+    runs = {}
+    for name in ("unfused", "fused"):
+        runs[name] = dict(lin=DelayedScalingLinear(hist_len=16), w=w0.clone(),
+                          m=torch.zeros_like(w0), v=torch.zeros_like(w0))
+    w_casts = []
+    orig_cast = runs["fused"]["lin"]._cast
+    runs["fused"]["lin"]._cast = lambda t, *a: (w_casts.append(t), orig_cast(t, *a))
+    for step in range(6):
+        xb, _, dyb = workloads.llama_tensors("k_proj", step, m=M)
+        x, dy = dev_bf16(xb), dev_bf16(dyb)
+        if step == NAN_STEP:
+            dy = dy.clone()
+            dy[3, 5] = float("nan")
+        outs = {}
+        for name, r in runs.items():
+            lin = r["lin"]
+            w_before = r["w"].clone()
+            o = lin.step(x, r["w"], dy)
+            outs[name] = {k: t.clone() for k, t in o.items()}
+            if name == "unfused":
+                dsg.fp8ds_adamw(r["w"], o["dw"], r["m"], r["v"], hp["lr"], hp["beta1"],
+                                hp["beta2"], hp["eps"], hp["weight_decay"], step + 1,
+                                grad_amax=lin.amax_dw)
+            else:
+                lin.adamw_step(r["w"], r["m"], r["v"], hp["lr"], step + 1, hp["beta1"],
+                               hp["beta2"], hp["eps"], hp["weight_decay"])
+            torch.cuda.synchronize()
+            assert torch.equal(r["w"], w_before) == (step == NAN_STEP), (name, step)
+        a, b = runs["unfused"], runs["fused"]
+        for k in ("xq", "wq", "wqt", "dyq"):
+            assert torch.equal(outs["unfused"][k], outs["fused"][k]), (step, k)
+        for k in ("y", "dx", "dw"):
+            assert torch.equal(outs["unfused"][k].view(torch.int16),
+                               outs["fused"][k].view(torch.int16)), (step, k)
+        for k in ("w", "m", "v"):
+            assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), (step, k)
+        for k in ("scale", "history", "cursor"):  # as bits: the dY history holds a NaN
+            assert torch.equal(getattr(a["lin"], k).view(torch.int32),
+                               getattr(b["lin"], k).view(torch.int32)), (step, k)
+        # amax[W] of the fused run already describes the next step's weights (its
+        # push into the history is compared above, one step later)
+        assert torch.equal(a["lin"].amax[0::2].view(torch.int32),
+                           b["lin"].amax[0::2].view(torch.int32)), step
+        assert b["lin"].amax[1].item() == b["w"].abs().max().item()
+    # the fused run cast W only in its first forward
+    assert w_casts.count(1) == 1
