@@ -277,13 +277,10 @@ __device__ __forceinline__ void tile_store_qt(const uint8_t* tile, uint8_t* __re
   }
 }
 
-// Parks the 16 codes of row r, columns cp .. cp + 15 of a tile in LDS with the
-// swizzle tile_store_qt reads.
-__device__ __forceinline__ void tile_park16(uint8_t* tile, int r, int cp, const u32x4& codes) {
+// Parks the 8 codes of row r, columns c .. c + 7 (c % 8 == 0): one 8-byte group.
+__device__ __forceinline__ void tile_park8(uint8_t* tile, int r, int c, const u32x2& codes) {
   constexpr int T = 128;
-  const int c8 = cp >> 3, sw = r & 7;  // two 8-byte column groups, swizzled
-  *reinterpret_cast<u32x2*>(tile + r * T + ((c8 ^ sw) << 3)) = u32x2{codes.x, codes.y};
-  *reinterpret_cast<u32x2*>(tile + r * T + (((c8 + 1) ^ sw) << 3)) = u32x2{codes.z, codes.w};
+  *reinterpret_cast<u32x2*>(tile + r * T + (((c >> 3) ^ (r & 7)) << 3)) = codes;
 }
 
 // Parks the 4 codes of row r, columns c .. c + 3 (c % 4 == 0) in the same layout.
