@@ -16,7 +16,9 @@ recorded between the launches on the stream the library launches on.
 
 The line also carries context figures that are not `value`: the same GEMMs on
 the FP8 matrix instructions (`fp8_mma_path_tflops`), the 2^30-element stress
-casts (`cast_stress`), and `configs`, the throughput of the other workloads
+casts (`cast_stress`), the fused AdamW step on the 4096 x 4096 weight that also
+writes the next forward's FP8 weights (`optimizer`, against the unfused update
+plus weight cast), and `configs`, the throughput of the other workloads
 (forward-only 4096 Linear at M = 8192, the decoder-layer projections at
 M = 8192, 512 small Linears).
 

@@ -95,7 +95,11 @@ def test_midpoints_and_neighbours(fmt):
     assert np.array_equal(q, ofp8.encode(pts, fmt))
 
 
-@pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 255, 4099])
+# Workgroups own 65536 elements in 16-byte pieces (8 BF16 / 4 FP32 elements) that
+# form 16-element groups with partners 1024 pieces apart: the larger sizes end in
+# a partial workgroup whose last pieces lack partners, plus a sub-piece tail.
+@pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 255, 4099, 65536 + 9, 65536 + 8 * 1024 + 5,
+                               3 * 65536 + 12345, (1 << 20) + 3])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_small_and_ragged_sizes(n, bf16):
     rng = np.random.default_rng(n)
