@@ -408,7 +408,7 @@ def main():
     gemms = ("gemm_fwd_nt", "gemm_dgrad_nt", "gemm_wgrad_tn")
     gemm_tflops = {n: round(flop_gemm / (avg[n] * 1e-3) / 1e12, 1) for n in gemms}
     # algorithmic bytes of the casts: read the input (2 B), write the FP8 bytes (1 B)
-    cast_bytes = {"cast_x": M * K * 3, "cast_w_t": K * N * 3, "cast_dy": M * N * 3}
+    cast_bytes = {"cast_x": M * K * 3, "cast_w_t": K * N * 4, "cast_dy": M * N * 3}
     cast_gbps = {n: round(b / (avg[n] * 1e-3) / 1e9, 1) for n, b in cast_bytes.items()}
     dom = max(gemms, key=lambda n: avg[n])
     achieved = flop_gemm / (avg[dom] * 1e-3) / 1e12
