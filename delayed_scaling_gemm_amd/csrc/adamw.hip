@@ -211,6 +211,7 @@ __global__ __launch_bounds__(256) void adamw_transpose_kernel(AdamWLaunch p) {
     const int tr = tid >> 1;        // row within the tile
     const int tc = (tid & 1) * 64;  // first of this thread's 64 columns
     const int64_t r = r0 + tr;
+#pragma unroll 1  // unrolled, this rarely used path would set the kernel's register count
     for (int i = 0; i < 64; ++i) {
       const int64_t c = c0 + tc + i;
       uint32_t code = 0;
@@ -226,6 +227,7 @@ __global__ __launch_bounds__(256) void adamw_transpose_kernel(AdamWLaunch p) {
     const int orr = (tid & 1) * 64;  // first of this thread's 64 rows
     const int64_t oc = c0 + oc_l;
     if (oc < cols) {
+#pragma unroll 1
       for (int i = 0; i < 64; ++i) {
         const int64_t orow = r0 + orr + i;
         if (orow < rows) p.qt[oc * rows + orow] = tile[(orr + i) * T + oc_l];

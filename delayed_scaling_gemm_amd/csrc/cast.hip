@@ -194,6 +194,9 @@ __global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastAr
 #define FP8DS_TRANSPOSE_TILES 1
 #endif
 constexpr int kTransposeTiles = FP8DS_TRANSPOSE_TILES;
+#ifndef FP8DS_TRANSPOSE_UNROLL
+#define FP8DS_TRANSPOSE_UNROLL 4
+#endif
 
 template <bool BF16, int FMT, bool STATS>
 __global__ __launch_bounds__(256) void cast_transpose_kernel(
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(
       // pieces of 16 input bytes (8 BF16 or 4 FP32 elements); pass i takes pieces
       // u = 256 (NP i + k) + tid of the tile, so a wave's loads cover whole row runs
       constexpr int PER = BF16 ? 8 : 4, NP = 16 / PER, PPR = T / PER;
-#pragma unroll
+#pragma unroll FP8DS_TRANSPOSE_UNROLL
       for (int i = 0; i < 4; ++i) {
         int rr[NP], cc[NP];
         int64_t off[NP];
@@ -259,6 +262,7 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(
       const int tr = tid >> 1;         // row within the tile
       const int tc = (tid & 1) * 64;   // first of this thread's 64 columns
       const int64_t r = r0 + tr;
+#pragma unroll 1  // unrolled, this rarely used path set the kernel's register count (157)
       for (int i = 0; i < 64; ++i) {
         const int64_t c = c0 + tc + i;
         uint32_t code = 0;
@@ -287,6 +291,7 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(
       const int orr = (tid & 1) * 64;  // first of this thread's 64 rows
       const int64_t oc = c0 + oc_l;
       if (oc < cols) {
+#pragma unroll 1
         for (int i = 0; i < 64; ++i) {
           const int64_t orow = r0 + orr + i;
           if (orow < rows) qt[oc * rows + orow] = tile[(orr + i) * T + oc_l];
