@@ -36,8 +36,11 @@ Parity status of each function (what pins it, see ``tests/test_oracle_*.py``):
   motion under a constant gradient, a 50-digit decimal evaluation of one step,
   the unscale and skip rules).
 * ``health.cast_health``: pinned (hand-worked E4M3 / E5M2 cases).
+* ``finer.*``: pinned (a hand-worked per-row E4M3 case in ``tests/golden/``,
+  power-of-two row invariance, the row maximum on FP8_MAX, degenerate rows, a
+  brute-force scaled GEMM in exact fractions, the per-tensor special case).
 * Parity unpinned: nothing in the oracle; on the GPU side the fp32 summation
   order of the accumulator is bounded, not pinned (see ``gemm.py``).
 """
 
-from . import adamw, amax, bf16, fp8, gemm, health, linear, scaling  # noqa: F401
+from . import adamw, amax, bf16, finer, fp8, gemm, health, linear, scaling  # noqa: F401
