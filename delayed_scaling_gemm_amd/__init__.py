@@ -66,6 +66,13 @@ def _declare(lib):
     lib.fp8ds_adamw.restype = i32
     lib.fp8ds_adamw.argtypes = [vp, vp, i32, vp, vp, i64, i64, f, f, f, f, f, f, i64, vp, i32, vp,
                                 vp, vp, vp, vp, vp, vp]
+    lib.fp8ds_cast_rowwise.restype = i32
+    lib.fp8ds_cast_rowwise.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp]
+    lib.fp8ds_cast_current.restype = i32
+    lib.fp8ds_cast_current.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.fp8ds_gemm_rowcol.restype = i32
+    lib.fp8ds_gemm_rowcol.argtypes = [i32, i32, i64, i64, i64, vp, i32, i64, vp, vp, i32, i64, vp,
+                                      vp, i32, i64, vp, vp]
     lib.fp8ds_gemm_batched.restype = i32
     lib.fp8ds_gemm_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i32, i64, i64, vp, vp, i32,
                                        i64, i64, vp, vp, i32, i64, i64, vp, i32, vp]
@@ -330,6 +337,62 @@ def fp8ds_adamw(w, g, m, v, lr, beta1, beta2, eps, weight_decay, step, grad_scal
                              float(weight_decay), float(grad_scale), int(step), _ptr(grad_amax),
                              fmt, _ptr(scale), _ptr(q), _ptr(q_t), _ptr(scale_used), _ptr(amax),
                              _ptr(sat_count), _stream(stream)))
+
+
+
+def fp8ds_cast_rowwise(x, fmt, margin, q, scale, scale_inv=None, amax=None, stream=None):
+    """Per-row current scaling of the 2-D ``x`` into ``q`` (uint8) with
+    ``scale`` / ``scale_inv`` / ``amax`` per row (fp32 device tensors of rows)."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    f32 = (torch.float32,)
+    _need(x, "x", (torch.bfloat16, torch.float32), rows * cols)
+    _need(q, "q", (torch.uint8,), rows * cols)
+    if scale is None:
+        raise ValueError("scale is required")
+    _need(scale, "scale", f32, rows)
+    _need(scale_inv, "scale_inv", f32, rows)
+    _need(amax, "amax", f32, rows)
+    _check(lib().fp8ds_cast_rowwise(_ptr(x), _dtype_code(x), rows, cols, fmt, int(margin), _ptr(q),
+                                    _ptr(scale), _ptr(scale_inv), _ptr(amax), _stream(stream)))
+
+
+def fp8ds_cast_current(x, fmt, margin, q, scale, amax, q_t=None, scale_inv=None, sat_count=None,
+                       stream=None):
+    """Per-tensor current scaling: amax of ``x``, its scale, then the cast."""
+    import torch
+
+    rows, cols = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.numel())
+    f32 = (torch.float32,)
+    _need(x, "x", (torch.bfloat16, torch.float32), rows * cols)
+    _need(q, "q", (torch.uint8,), rows * cols)
+    _need(q_t, "q_t", (torch.uint8,), rows * cols)
+    if scale is None or amax is None:
+        raise ValueError("scale and amax are required")
+    _need(scale, "scale", f32, 1)
+    _need(amax, "amax", f32, 1)
+    _need(scale_inv, "scale_inv", f32, 1)
+    _need(sat_count, "sat_count", (torch.int64,), 1)
+    _check(lib().fp8ds_cast_current(_ptr(x), _dtype_code(x), rows, cols, fmt, int(margin), _ptr(q),
+                                    _ptr(q_t), _ptr(scale), _ptr(scale_inv), _ptr(amax),
+                                    _ptr(sat_count), _stream(stream)))
+
+
+def fp8ds_gemm_rowcol(opa, opb, M, N, K, a, fa, lda, scale_inv_a, b, fb, ldb, scale_inv_b, c, ldc,
+                      amax_c=None, stream=None):
+    """GEMM with an inverse scale per row of op(A) (``scale_inv_a`` [M]) and per
+    column of op(B) (``scale_inv_b`` [N]); exact datapath."""
+    import torch
+
+    _check_gemm(opa, opb, M, N, K, 1, a, lda, 0, None, b, ldb, 0, None, c, ldc, 0, amax_c)
+    _need(scale_inv_a, "scale_inv_a", (torch.float32,), M)
+    _need(scale_inv_b, "scale_inv_b", (torch.float32,), N)
+    _check(lib().fp8ds_gemm_rowcol(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_inv_a), _ptr(b),
+                                   fb, ldb, _ptr(scale_inv_b), _ptr(c), _dtype_code(c), ldc,
+                                   _ptr(amax_c), _stream(stream)))
 
 
 def abi_version() -> int:

@@ -199,7 +199,8 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
                        int64_t stride_a, const float* scale_a, const uint8_t* B, fp8ds_format fb,
                        int64_t ldb, int64_t stride_b, const float* scale_b, void* C,
                        fp8ds_dtype ct, int64_t ldc, int64_t stride_c, float* amax_c,
-                       fp8ds_mma mma, hipStream_t stream) {
+                       fp8ds_mma mma, hipStream_t stream, bool rowcol = false) {
+  // rowcol: scale_a / scale_b are inverse-scale vectors [M] / [N] (exact datapath)
   if (mma != FP8DS_MMA_EXACT && mma != FP8DS_MMA_FP8)
     return fail(FP8DS_ERR_ENUM, "%s: bad mma %d", who, (int)mma);
   if ((opa != FP8DS_OP_N && opa != FP8DS_OP_T) || (opb != FP8DS_OP_N && opb != FP8DS_OP_T))
@@ -231,7 +232,9 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
                 "%lld, ldc %lld >= %lld)", who, (long long)lda, (long long)a_cols, (long long)ldb,
                 (long long)b_cols, (long long)ldc, (long long)N);
   if (!C || !scale_a || !scale_b || (K > 0 && (!A || !B)))
-    return fail(FP8DS_ERR_NULL, "%s: A, B, C, scale_a and scale_b are required", who);
+    return fail(FP8DS_ERR_NULL, "%s: A, B, C and the two scales are required", who);
+  if (rowcol && !aligned16(scale_b))
+    return fail(FP8DS_ERR_ALIGN, "%s: scale_inv_b must be 16-byte aligned", who);
   const int esz = ct == FP8DS_BF16 ? 2 : 4;
   if ((K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16)) || !aligned16(C) ||
       (ldc * esz) % 16)
@@ -250,8 +253,14 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
     p.B = B; p.fb = (int)fb; p.ldb = ldb; p.scale_b = scale_b;
     p.C = C; p.out_bf16 = ct == FP8DS_BF16; p.ldc = ldc; p.amax_c = amax_c;
     p.batch = batch; p.stride_a = stride_a; p.stride_b = stride_b; p.stride_c = stride_c;
-    e = mma == FP8DS_MMA_EXACT ? fp8ds::launch_gemm_exact(p, num_cus(), stream)
-                               : fp8ds::launch_gemm_fp8(p, num_cus(), stream);
+    if (rowcol) {
+      p.inv_a = scale_a;
+      p.inv_b = scale_b;
+      e = fp8ds::launch_gemm_rowcol(p, num_cus(), stream);
+    } else {
+      e = mma == FP8DS_MMA_EXACT ? fp8ds::launch_gemm_exact(p, num_cus(), stream)
+                                 : fp8ds::launch_gemm_fp8(p, num_cus(), stream);
+    }
   }
   return hip_status(e, who);
 }
@@ -325,6 +334,75 @@ int fp8ds_adamw(float* w, const void* g, fp8ds_dtype gt, float* m, float* v, int
   hipError_t e = hipSuccess;
   if (cast) e = fp8ds::launch_prologue(1, scale, scale_used, amax, sat_count, stream);
   if (e == hipSuccess && n > 0) e = fp8ds::launch_adamw(a, stream);
+  return hip_status(e, who);
+}
+
+int fp8ds_gemm_rowcol(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* A, fp8ds_format fa, int64_t lda, const float* scale_inv_a,
+                      const uint8_t* B, fp8ds_format fb, int64_t ldb, const float* scale_inv_b,
+                      void* C, fp8ds_dtype ct, int64_t ldc, float* amax_c, hipStream_t stream) {
+  return gemm_common("fp8ds_gemm_rowcol", opa, opb, M, N, K, 1, A, fa, lda, 0, scale_inv_a, B, fb,
+                     ldb, 0, scale_inv_b, C, ct, ldc, 0, amax_c, FP8DS_MMA_EXACT, stream, true);
+}
+
+int fp8ds_cast_rowwise(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+                       int margin, uint8_t* q, float* scale, float* scale_inv, float* amax,
+                       hipStream_t stream) {
+  const char* who = "fp8ds_cast_rowwise";
+  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "%s: bad dtype %d", who, (int)xt);
+  if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "%s: bad format %d", who, (int)fmt);
+  if (rows < 0 || cols < 0 || rows >= (int64_t(1) << 31) || (cols > 0 && rows > kMaxElems / cols))
+    return fail(FP8DS_ERR_SHAPE, "%s: bad shape %lld x %lld", who, (long long)rows,
+                (long long)cols);
+  if (margin < -126 || margin > 126)
+    return fail(FP8DS_ERR_SHAPE, "%s: margin %d not in [-126, 126]", who, margin);
+  if (rows > 0 && !scale) return fail(FP8DS_ERR_NULL, "%s: scale is null", who);
+  if (rows * cols > 0) {
+    if (!x || !q) return fail(FP8DS_ERR_NULL, "%s: x or q is null", who);
+    if (!aligned16(x) || !aligned16(q))
+      return fail(FP8DS_ERR_ALIGN, "%s: x and q must be 16-byte aligned", who);
+  }
+  return hip_status(fp8ds::launch_rowwise_cast(x, xt == FP8DS_BF16, rows, cols, (int)fmt, margin,
+                                               q, scale, scale_inv, amax, stream),
+                    who);
+}
+
+int fp8ds_cast_current(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols,
+                       fp8ds_format fmt, int margin, uint8_t* q, uint8_t* q_t, float* scale,
+                       float* scale_inv, float* amax, uint64_t* sat_count, hipStream_t stream) {
+  const char* who = "fp8ds_cast_current";
+  if (!scale || !amax) return fail(FP8DS_ERR_NULL, "%s: scale and amax are required", who);
+  if (margin < -126 || margin > 126)
+    return fail(FP8DS_ERR_SHAPE, "%s: margin %d not in [-126, 126]", who, margin);
+  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "%s: bad dtype %d", who, (int)xt);
+  if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "%s: bad format %d", who, (int)fmt);
+  if (rows < 0 || cols < 0 || (cols > 0 && rows > kMaxElems / cols))
+    return fail(FP8DS_ERR_SHAPE, "%s: bad shape %lld x %lld", who, (long long)rows,
+                (long long)cols);
+  const int64_t n = rows * cols;
+  if (n > 0) {
+    if (!x || !q) return fail(FP8DS_ERR_NULL, "%s: x or q is null", who);
+    if (!aligned16(x) || !aligned16(q) || (q_t && !aligned16(q_t)))
+      return fail(FP8DS_ERR_ALIGN, "%s: x, q and q_t must be 16-byte aligned", who);
+  }
+  if (q_t && (rows + 127) / 128 > 65535)
+    return fail(FP8DS_ERR_SHAPE, "%s: a transposed copy supports at most %d rows", who,
+                65535 * 128);
+  // amax pass, scale from it, then the cast with that scale
+  hipError_t e = fp8ds::launch_prologue(1, nullptr, nullptr, amax, sat_count, stream);
+  if (e == hipSuccess && n > 0)
+    e = fp8ds::launch_cast(x, xt == FP8DS_BF16, 1, n, n, 0, nullptr, nullptr, n, amax, nullptr,
+                           nullptr, num_cus(), stream);
+  if (e == hipSuccess) e = fp8ds::launch_current_scale(amax, (int)fmt, margin, scale, scale_inv,
+                                                       stream);
+  if (e == hipSuccess && n > 0) {
+    if (q_t)
+      e = fp8ds::launch_cast_transpose(x, xt == FP8DS_BF16, rows, cols, (int)fmt, scale, q, q_t,
+                                       nullptr, sat_count, nullptr, stream);
+    else
+      e = fp8ds::launch_cast(x, xt == FP8DS_BF16, 1, n, n, (int)fmt, scale, q, n, nullptr,
+                             sat_count, nullptr, num_cus(), stream);
+  }
   return hip_status(e, who);
 }
 

@@ -83,5 +83,18 @@ __device__ __forceinline__ uint32_t canonical_amax_bits(uint32_t m) {
   return m > 0x7F800000u ? 0x7FC00000u : m;
 }
 
+// Scale from an amax or window value w ("LLM FP8 微调上线生产实战" §核心原理: scale =
+// (FP8_MAX / amax) / 2^margin): one correctly rounded fp32 division and an exact
+// power-of-two rescale (rounded only if subnormal); 1.0 unless w and the result are
+// finite and positive (NaN fails every comparison).
+__device__ __forceinline__ float scale_from_amax(float w, float fmax, int margin) {
+  float s = 1.0f;
+  if (w > 0.0f && w <= __uint_as_float(0x7F7FFFFFu)) {
+    const float sc = ldexpf(__fdiv_rn(fmax, w), -margin);
+    if (sc > 0.0f && sc <= __uint_as_float(0x7F7FFFFFu)) s = sc;
+  }
+  return s;
+}
+
 
 }  // namespace fp8ds

@@ -73,6 +73,8 @@ struct GemmArgs {
   int64_t stride_a, stride_b, stride_c;
   int tiles_m, tiles_n;
   int out_f32;
+  const float* inv_a;  // VS: inverse scale per row of op(A) [M]
+  const float* inv_b;  // VS: inverse scale per column of op(B) [N]
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 4)) & 7; }
@@ -406,6 +408,7 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 // included; a NaN stays a quiet NaN of its sign).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
@@ -419,7 +422,15 @@ __device__ __forceinline__ u16x2_t abs_bf16x2(uint32_t v) {
 // for g = 0..3 (accumulator elements 4g .. 4g+3).  Tiles inside the matrix take
 // a branch-free path (row pointers per block row, immediate column offsets);
 // edge tiles check every row and group of four columns.
-template <int BM, int BN, int FM, int FN, int WTM, int WTN>
+// VS (scale vectors): y = fl32(fl32(acc * inv_a[row]) * inv_b[col]) instead of
+// fl32(acc * d); a lane loads its rows' factors once and four columns' factors
+// with one 16-byte load per group.
+template <bool VS>
+__device__ __forceinline__ float dq(float a, float r, float c) {
+  if constexpr (VS) return (a * r) * c;
+  else return a * r;
+}
+template <int BM, int BN, int FM, int FN, int WTM, int WTN, bool VS = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM][FN], int64_t m0,
                                          int64_t n0, int wm, int wn, int tid, int64_t bz, float d,
                                          uint32_t* red) {
@@ -436,12 +447,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         uint16_t* row = C + (mb + i * 32) * p.ldc + nb;
+        const float r = VS ? p.inv_a[mb + i * 32] : d;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const uint32_t lo = pack_bf16x2(acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d);
-            const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d);
+            f32x4_t c = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (VS) c = *reinterpret_cast<const f32x4_t*>(p.inv_b + nb + j * 32 + 8 * g);
+            const uint32_t lo = pack_bf16x2(dq<VS>(acc[i][j][4 * g], r, c[0]),
+                                            dq<VS>(acc[i][j][4 * g + 1], r, c[1]));
+            const uint32_t hi = pack_bf16x2(dq<VS>(acc[i][j][4 * g + 2], r, c[2]),
+                                            dq<VS>(acc[i][j][4 * g + 3], r, c[3]));
             *reinterpret_cast<u32x2*>(row + j * 32 + 8 * g) = u32x2{lo, hi};
             am2 = __builtin_elementwise_max(am2, __builtin_elementwise_max(abs_bf16x2(lo), abs_bf16x2(hi)));
           }
@@ -453,15 +469,23 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
         const int64_t m = mb + i * 32;
         if (m >= M) continue;
         uint16_t* row = C + m * p.ldc;
+        const float r = VS ? p.inv_a[m] : d;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int64_t n = nb + j * 32 + 8 * g;
             if (n >= N) continue;
-            const uint32_t lo = pack_bf16x2(acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d);
-            const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d);
             const int64_t left = N - n;  // >= 1
+            f32x4_t c = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (VS) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v) c[v] = v < left ? p.inv_b[n + v] : 0.f;
+            }
+            const uint32_t lo = pack_bf16x2(dq<VS>(acc[i][j][4 * g], r, c[0]),
+                                            dq<VS>(acc[i][j][4 * g + 1], r, c[1]));
+            const uint32_t hi = pack_bf16x2(dq<VS>(acc[i][j][4 * g + 2], r, c[2]),
+                                            dq<VS>(acc[i][j][4 * g + 3], r, c[3]));
             const uint32_t mlo = left >= 2 ? 0x7FFF7FFFu : 0x7FFFu;
             const uint32_t mhi = left >= 4 ? 0x7FFF7FFFu : left == 3 ? 0x7FFFu : 0u;
             const u16x2_t m2 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, lo & mlo),
@@ -484,6 +508,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
       const int64_t m = mb + i * 32;
       if (!full && m >= M) continue;
       float* row = C + m * p.ldc;
+      const float r = VS ? p.inv_a[m] : d;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -493,7 +518,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
           float y[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            y[v] = acc[i][j][4 * g + v] * d;
+            float c = 1.f;
+            if constexpr (VS) c = (full || n + v < N) ? p.inv_b[n + v] : 0.f;
+            y[v] = dq<VS>(acc[i][j][4 * g + v], r, c);
             if (full || n + v < N) amax = max(amax, __float_as_uint(y[v]) & 0x7FFFFFFFu);
           }
           if (full || n + 3 < N) {
@@ -537,7 +564,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
 //     under step 7.
 // FP8: a stage is 2 MFMA steps of K = 64 (32x32x64 F8F6F4), each on two chunks.
 
-template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT>
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT,
+          bool VS = false>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   constexpr int NT = 256;
   constexpr int WTM = BM / 2, WTN = BN / 2;
@@ -572,7 +600,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int nk = (int)((K + KB - 1) / KB);
-  const float d = __fdiv_rn(1.0f, p.scale_a[bz] * p.scale_b[bz]);  // dequant factor
+  // dequant factor (VS: the per-row / per-column factors are applied in the epilogue)
+  const float d = VS ? 1.0f : __fdiv_rn(1.0f, p.scale_a[bz] * p.scale_b[bz]);
   const int fr = lane & 31;
   const int fc = (lane >> 5) * 4;  // first of this lane's four chunks
 
@@ -812,12 +841,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     if (nk > 0) stage(nk - 1, std::false_type{});
   }
 
-  epilogue<BM, BN, FM, FN, WTM, WTN>(p, acc, m0, n0, wm, wn, tid, bz, d, red);
+  epilogue<BM, BN, FM, FN, WTM, WTN, VS>(p, acc, m0, n0, wm, wn, tid, bz, d, red);
 }
 
 // ------------------------------------------------------------------ dispatch
 
-template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT>
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT, bool VS>
 static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   GemmArgs a;
   a.M = q.M; a.N = q.N; a.K = q.K;
@@ -828,15 +857,17 @@ static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   a.tiles_m = (int)((q.M + BM - 1) / BM);
   a.tiles_n = (int)((q.N + BN - 1) / BN);
   a.out_f32 = q.out_bf16 ? 0 : 1;
+  a.inv_a = q.inv_a;
+  a.inv_b = q.inv_b;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)q.batch);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, EXACT, DIRECT>), grid, dim3(256), 0,
-                     stream, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, EXACT, DIRECT, VS>), grid, dim3(256),
+                     0, stream, a);
   return hipGetLastError();
 }
 
 // K a multiple of the stage depth and operands in aligned 16-byte chunks: LDS is
 // filled by direct loads; otherwise through registers.
-template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT>
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool VS>
 static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream) {
   {
     // Direct loads move aligned 16-byte chunks; MN-contiguous operands are
@@ -848,36 +879,36 @@ static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream) {
     const bool a_ok = aligned(q.A, q.lda, q.stride_a) && (A_KC || q.M % 16 == 0);
     const bool b_ok = aligned(q.B, q.ldb, q.stride_b) && (B_KC || q.N % 16 == 0);
     if (q.K % 128 == 0 && a_ok && b_ok)
-      return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, true>(q, stream);
+      return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, true, VS>(q, stream);
   }
-  return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, false>(q, stream);
+  return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, false, VS>(q, stream);
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC, bool EXACT>
+template <int BM, int BN, bool A_KC, bool B_KC, bool EXACT, bool VS>
 static hipError_t launch_layout(const GemmProblem& q, hipStream_t s) {
-  if (q.fa == kE4M3 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE4M3, EXACT>(q, s);
-  if (q.fa == kE4M3 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE5M2, EXACT>(q, s);
-  if (q.fa == kE5M2 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE4M3, EXACT>(q, s);
-  if (q.fa == kE5M2 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE5M2, EXACT>(q, s);
+  if (q.fa == kE4M3 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE4M3, EXACT, VS>(q, s);
+  if (q.fa == kE4M3 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE5M2, EXACT, VS>(q, s);
+  if (q.fa == kE5M2 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE4M3, EXACT, VS>(q, s);
+  if (q.fa == kE5M2 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE5M2, EXACT, VS>(q, s);
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, bool EXACT>
+template <int BM, int BN, bool EXACT, bool VS>
 static hipError_t launch_tile(const GemmProblem& q, hipStream_t s) {
-  if (q.opa == 0 && q.opb == 0) return launch_layout<BM, BN, true, false, EXACT>(q, s);  // NN
-  if (q.opa == 0 && q.opb == 1) return launch_layout<BM, BN, true, true, EXACT>(q, s);   // NT
-  if (q.opa == 1 && q.opb == 0) return launch_layout<BM, BN, false, false, EXACT>(q, s); // TN
+  if (q.opa == 0 && q.opb == 0) return launch_layout<BM, BN, true, false, EXACT, VS>(q, s);  // NN
+  if (q.opa == 0 && q.opb == 1) return launch_layout<BM, BN, true, true, EXACT, VS>(q, s);   // NT
+  if (q.opa == 1 && q.opb == 0) return launch_layout<BM, BN, false, false, EXACT, VS>(q, s); // TN
   return hipErrorInvalidValue;
 }
 
 // Tile choice: 256 x 256 tiles when they alone give every CU at least one tile,
 // else 128 x 128 tiles.
-template <bool EXACT>
+template <bool EXACT, bool VS = false>
 static hipError_t launch_path(const GemmProblem& q, int num_cus, hipStream_t stream) {
   if (q.M <= 0 || q.N <= 0 || q.batch <= 0) return hipSuccess;
   const int64_t big_tiles = ((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
-  if (big_tiles >= num_cus) return launch_tile<256, 256, EXACT>(q, stream);
-  return launch_tile<128, 128, EXACT>(q, stream);
+  if (big_tiles >= num_cus) return launch_tile<256, 256, EXACT, VS>(q, stream);
+  return launch_tile<128, 128, EXACT, VS>(q, stream);
 }
 
 }  // namespace fp8ds

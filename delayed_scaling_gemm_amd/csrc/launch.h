@@ -53,6 +53,15 @@ struct AdamWLaunch {
 };
 hipError_t launch_adamw(const AdamWLaunch& a, hipStream_t stream);
 
+// Current scaling with one scale per row of a [rows x cols] matrix: q, scale[rows],
+// scale_inv[rows] (or null), amax[rows] (or null).
+hipError_t launch_rowwise_cast(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
+                               int margin, uint8_t* q, float* scale, float* scale_inv,
+                               float* amax, hipStream_t stream);
+// scale[0] (and scale_inv[0], or null) from amax[0] by the scale formula.
+hipError_t launch_current_scale(const float* amax, int fmt, int margin, float* scale,
+                                float* scale_inv, hipStream_t stream);
+
 // History push + window reduction + next scale for n tensors.
 // fmt_bits: bit t set = tensor t is E5M2.
 struct FmtBits {
@@ -80,10 +89,15 @@ struct GemmProblem {
   float* amax_c;  // reset by the caller
   int64_t batch;
   int64_t stride_a, stride_b, stride_c;  // bytes, bytes, elements
+  const float* inv_a = nullptr;  // scale vectors (launch_gemm_rowcol): [M], [N]
+  const float* inv_b = nullptr;
 };
 // EXACT datapath: FP8 widened to F16, F16 MFMA, FP32 sums.
 hipError_t launch_gemm_exact(const GemmProblem& p, int num_cus, hipStream_t stream);
 // FP8 datapath: native FP8 MFMA (hardware summation precision).
 hipError_t launch_gemm_fp8(const GemmProblem& p, int num_cus, hipStream_t stream);
+// EXACT datapath with one inverse scale per row of op(A) and per column of op(B)
+// (p.inv_a, p.inv_b; batch 1).
+hipError_t launch_gemm_rowcol(const GemmProblem& p, int num_cus, hipStream_t stream);
 
 }  // namespace fp8ds

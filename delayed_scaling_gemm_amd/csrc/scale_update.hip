@@ -53,12 +53,7 @@ __global__ __launch_bounds__(64) void scale_update_kernel(int n, int hist_len,
   float w = (algo == 0) ? (any_nan ? __uint_as_float(0x7FC00000u) : m) : a;
   const bool e5m2 = (fmt.w[t >> 5] >> (t & 31)) & 1u;
   const float fmax = e5m2 ? FmtTraits<kE5M2>::kMax : FmtTraits<kE4M3>::kMax;
-  float s = 1.0f;
-  if (w > 0.0f && w <= __uint_as_float(0x7F7FFFFFu)) {  // finite and positive (NaN fails)
-    float qt = __fdiv_rn(fmax, w);   // one correctly rounded fp32 division
-    float sc = ldexpf(qt, -margin);  // exact power-of-two rescale (rounds only if subnormal)
-    if (sc > 0.0f && sc <= __uint_as_float(0x7F7FFFFFu)) s = sc;
-  }
+  const float s = scale_from_amax(w, fmax, margin);
   scale[t] = s;
   if (scale_inv) scale_inv[t] = __fdiv_rn(1.0f, s);
 }

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FP8DS_ABI_VERSION 4
+#define FP8DS_ABI_VERSION 5
 
 typedef enum {
   FP8DS_OK = 0,
@@ -306,6 +306,72 @@ int fp8ds_adamw(float* w, const void* g, fp8ds_dtype gt, float* m, float* v, int
                 float grad_scale, int64_t step, const float* grad_amax, fp8ds_format fmt,
                 const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
                 uint64_t* sat_count, hipStream_t stream);
+
+/*
+ * Finer-grained scaling: current (just-in-time) scales and one scale per row.
+ * [P2] §"FBGEMM_GPU 底层优化" (per-tensor, per-channel and per-token FP8 GEMM modes:
+ * FP8 operands, FP32 accumulation, BF16 output); the scale formula of [P3]
+ * §核心原理 "Scale 决定数值是否进入可表示区间" applied to the amax of what is being
+ * cast, with no history ([P3]'s reference list names current scaling beside
+ * delayed scaling).  In every case
+ *   s = ldexp(fl32(FP8_MAX(fmt) / a), -margin)  if a and the result are finite and
+ *       > 0, else 1.0;        scale_inv = fl32(1 / s)
+ * with a the amax of the tensor (current) or of the row (per row).
+ */
+
+/*
+ * fp8ds_cast_rowwise -- per-row current scaling of a [rows x cols] matrix:
+ *   a_r = max_c |x[r][c]|,  s_r from a_r as above,  q[r][c] = encode(fl32(x[r][c] * s_r)).
+ * Per-token scaling of activations X [M x K] is this call on X; per-channel
+ * scaling of a weight W [K x N] (a scale per output channel) is this call on
+ * W^T [N x K], the K-contiguous layout the forward GEMM reads with op T.
+ *
+ *   x          device, rows*cols elements of `xt`, row-major, 16-byte aligned.
+ *   rows       0 .. 2^31 - 1.   cols >= 0.
+ *   margin     integer exponent, -126..126.
+ *   q          device, rows*cols bytes, 16-byte aligned.
+ *   scale      device [rows] fp32 (required when rows > 0).
+ *   scale_inv  device [rows] or NULL: fl32(1 / scale[r]) -- the GEMM's row/column factors.
+ *   amax       device [rows] or NULL: a_r (NaN as fp8ds_amax).
+ */
+int fp8ds_cast_rowwise(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+                       int margin, uint8_t* q, float* scale, float* scale_inv, float* amax,
+                       hipStream_t stream);
+
+/*
+ * fp8ds_cast_current -- per-tensor current scaling: the amax of x, the scale from
+ * it, then fp8ds_cast with that scale (three passes: amax, scale, cast).
+ *
+ *   x, xt, rows, cols, fmt, q, q_t  as fp8ds_cast.    margin  -126..126.
+ *   scale      device, 1 float (required): receives s.
+ *   scale_inv  device or NULL: receives fl32(1 / s).
+ *   amax       device, 1 float (required): receives the amax of x.
+ *   sat_count  device or NULL: as fp8ds_cast (non-zero only for margin < 0).
+ */
+int fp8ds_cast_current(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols,
+                       fp8ds_format fmt, int margin, uint8_t* q, uint8_t* q_t, float* scale,
+                       float* scale_inv, float* amax, uint64_t* sat_count, hipStream_t stream);
+
+/*
+ * fp8ds_gemm_rowcol -- fp8ds_gemm with one scale per row of op(A) and per column
+ * of op(B) (per-token x per-channel), exact datapath:
+ *   C[i][j] = convert_ct( fl32( fl32(acc[i][j] * scale_inv_a[i]) * scale_inv_b[j] ) )
+ * with acc as fp8ds_gemm (FP32 accumulation of the decoded FP8 products).
+ *
+ *   scale_inv_a  device [M] fp32: inverse scale of each row of op(A) (e.g. the
+ *                scale_inv of fp8ds_cast_rowwise on X).
+ *   scale_inv_b  device [N] fp32, 16-byte aligned: inverse scale of each column of
+ *                op(B) (e.g. fp8ds_cast_rowwise on W^T).  A per-tensor scale is
+ *                passed as a vector of equal values.
+ *   Other arguments as fp8ds_gemm (no batch, no datapath choice).
+ * A scale that varies along K cannot be taken out of the sum: the products whose
+ * contraction runs along the scaled dimension need operands cast in the other
+ * orientation.
+ */
+int fp8ds_gemm_rowcol(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* A, fp8ds_format fa, int64_t lda, const float* scale_inv_a,
+                      const uint8_t* B, fp8ds_format fb, int64_t ldb, const float* scale_inv_b,
+                      void* C, fp8ds_dtype ct, int64_t ldc, float* amax_c, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(dsg.LIB_PATH)
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert dsg.abi_version() == 4
+    assert dsg.abi_version() == 5
 
 
 def test_status_strings():
@@ -121,3 +121,27 @@ def test_adamw_validation_errors_without_gpu():
     assert call(g=p + 4)[0] == -4
     assert call(q_t=p + 8)[0] == -4
     assert call(rows=65535 * 128 + 1, cols=1, q_t=p)[0] == -2
+
+
+def test_finer_scaling_validation_errors_without_gpu():
+    L = dsg.lib()
+    p = 0x1000
+    # fp8ds_cast_rowwise(x, xt, rows, cols, fmt, margin, q, scale, scale_inv, amax, stream)
+    assert L.fp8ds_cast_rowwise(p, 5, 4, 16, 0, 0, p, p, None, None, None) == -3
+    assert L.fp8ds_cast_rowwise(p, 1, 4, 16, 9, 0, p, p, None, None, None) == -3
+    assert L.fp8ds_cast_rowwise(p, 1, -4, 16, 0, 0, p, p, None, None, None) == -2
+    assert L.fp8ds_cast_rowwise(p, 1, 1 << 31, 1, 0, 0, p, p, None, None, None) == -2
+    assert L.fp8ds_cast_rowwise(p, 1, 4, 16, 0, 200, p, p, None, None, None) == -2
+    assert L.fp8ds_cast_rowwise(p, 1, 4, 16, 0, 0, p, None, None, None, None) == -1
+    assert L.fp8ds_cast_rowwise(p, 1, 4, 16, 0, 0, p + 4, p, None, None, None) == -4
+    # fp8ds_cast_current(x, xt, rows, cols, fmt, margin, q, q_t, scale, scale_inv, amax, sat, s)
+    assert L.fp8ds_cast_current(p, 1, 4, 16, 0, 0, p, None, None, None, p, None, None) == -1
+    assert L.fp8ds_cast_current(p, 1, 4, 16, 0, 0, p, None, p, None, None, None, None) == -1
+    assert L.fp8ds_cast_current(p, 1, 4, 16, 0, -127, p, None, p, None, p, None, None) == -2
+    assert L.fp8ds_cast_current(p, 1, 4, 16, 0, 0, p, p + 2, p, None, p, None, None) == -4
+    # fp8ds_gemm_rowcol: TT, misaligned scale_inv_b, null scales
+    g = lambda opa, opb, sa=p, sb=p: L.fp8ds_gemm_rowcol(opa, opb, 64, 64, 64, p, 0, 64, sa, p, 0,
+                                                        64, sb, p, 1, 64, None, None)
+    assert g(1, 1) == -6
+    assert g(0, 1, sb=p + 4) == -4
+    assert g(0, 1, sa=None) == -1
