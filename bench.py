@@ -16,9 +16,10 @@ recorded between the launches on the stream the library launches on.
 
 The line also carries context figures that are not `value`: the same GEMMs on
 the FP8 matrix instructions (`fp8_mma_path_tflops`), the 2^30-element stress
-casts (`cast_stress`), the fused AdamW step on the 4096 x 4096 weight that also
-writes the next forward's FP8 weights (`optimizer`, against the unfused update
-plus weight cast), and `configs`, the throughput of the other workloads
+casts (`cast_stress`), per-token / per-channel / current scaling of the same
+Linear's forward (`finer_scaling`), the fused AdamW step on the 4096 x 4096
+weight that also writes the next forward's FP8 weights (`optimizer`, against
+the unfused update plus weight cast), and `configs`, the throughput of the other workloads
 (forward-only 4096 Linear at M = 8192, the decoder-layer projections at
 M = 8192, 512 small Linears).
 
@@ -64,6 +65,8 @@ def parse():
                     help="skip the per-configuration throughput report")
     ap.add_argument("--no-optimizer", action="store_true",
                     help="skip the fused AdamW + weight-cast measurement")
+    ap.add_argument("--no-finer", action="store_true",
+                    help="skip the per-token / per-channel / current scaling measurement")
     ap.add_argument("--no-fp8-path", action="store_true",
                     help="skip the context timing of the FP8-MFMA datapath")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -236,6 +239,56 @@ def optimizer_report(torch, dsg, workloads, dev, rows=4096, cols=4096, iters=10)
     out["unfused_ms"] = round(unfused, 4)
     out["fused_speedup"] = round(unfused / t["fused"], 3)
     del wd, md, vd, g, q, qt
+    torch.cuda.empty_cache()
+    return out
+
+
+def finer_report(torch, dsg, x, w, iters=10):
+    """Finer-grained scaling on the benchmarked Linear's forward operands: the
+    per-token cast of X [M x K] (a scale per row; 3 B/element, read once), the
+    per-channel cast of W^T [N x K] (a scale per output channel), the per-tensor
+    current cast of X (amax pass, then the cast: 5 B/element) and the forward
+    GEMM with per-row x per-column dequant factors (2 M N K flop)."""
+    print("[bench] finer scaling: per-token / per-channel / current", file=sys.stderr, flush=True)
+    dev = x.device
+    M, K = x.shape
+    N = w.shape[1]
+    wt = w.t().contiguous()  # [N x K]: one row per output channel
+    xq = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    wq = torch.empty(N, K, dtype=torch.uint8, device=dev)
+    sx, ix, ax = (torch.empty(M, dtype=torch.float32, device=dev) for _ in range(3))
+    sw, iw, aw = (torch.empty(N, dtype=torch.float32, device=dev) for _ in range(3))
+    s1, i1, a1 = (torch.empty(1, dtype=torch.float32, device=dev) for _ in range(3))
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    amax_y = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "per_token_cast_x": (lambda: dsg.fp8ds_cast_rowwise(x, dsg.E4M3, 0, xq, sx, ix, ax),
+                             3.0 * M * K),
+        "per_channel_cast_wt": (lambda: dsg.fp8ds_cast_rowwise(wt, dsg.E4M3, 0, wq, sw, iw, aw),
+                                3.0 * N * K),
+        "current_cast_x": (lambda: dsg.fp8ds_cast_current(x, dsg.E4M3, 0, xq, s1, a1,
+                                                          scale_inv=i1), 5.0 * M * K),
+    }
+    out = {"shape": [M, K, N], "fmt": "e4m3"}
+    for name, (fn, nbytes) in calls.items():
+        fn()
+        ms = time_launches(torch, stream, fn, iters)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                     "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+    dsg.fp8ds_cast_rowwise(x, dsg.E4M3, 0, xq, sx, ix, ax)
+
+    def gemm():
+        dsg.fp8ds_gemm_rowcol(dsg.OP_N, dsg.OP_T, M, N, K, xq, dsg.E4M3, K, ix, wq, dsg.E4M3, K,
+                              iw, y, N, amax_y)
+
+    gemm()
+    ms = time_launches(torch, stream, gemm, iters)
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    out["rowcol_gemm_fwd_nt"] = {"ms": round(ms, 4), "TFLOP/s": round(tflops, 1),
+                                 "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4)}
+    del wt, xq, wq, y
     torch.cuda.empty_cache()
     return out
 
@@ -481,6 +534,9 @@ def main():
             fp8[n] = round(flop_gemm / (ms * 1e-3) / 1e12, 1)
         result["fp8_mma_path_tflops"] = fp8
 
+    if not args.no_finer:
+        x0, w0, _ = sets[0]
+        result["finer_scaling"] = finer_report(torch, dsg, x0, w0)
     if not args.no_stress:
         result["cast_stress"] = stress_cast(torch, dsg, workloads, dev)
     if not args.no_optimizer:
