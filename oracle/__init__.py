@@ -39,8 +39,13 @@ Parity status of each function (what pins it, see ``tests/test_oracle_*.py``):
 * ``finer.*``: pinned (a hand-worked per-row E4M3 case in ``tests/golden/``,
   power-of-two row invariance, the row maximum on FP8_MAX, degenerate rows, a
   brute-force scaled GEMM in exact fractions, the per-tensor special case).
+* ``mx.*``: pinned (hand-worked blocks of both formats in ``tests/golden/``,
+  E8M0 code values, power-of-two shifts, the largest element in the top binade,
+  a brute-force nearest-value search for every element, block independence,
+  zero/NaN/Inf blocks, the unit-scale GEMM equal to ``gemm.gemm_exact`` and an
+  exact-fraction triple loop).
 * Parity unpinned: nothing in the oracle; on the GPU side the fp32 summation
   order of the accumulator is bounded, not pinned (see ``gemm.py``).
 """
 
-from . import adamw, amax, bf16, finer, fp8, gemm, health, linear, scaling  # noqa: F401
+from . import adamw, amax, bf16, finer, fp8, gemm, health, linear, mx, scaling  # noqa: F401
