@@ -33,9 +33,9 @@ one written in the design notes):
 
 * ``E`` is clamped to the E8M0 range [-127, 127].  A block of zeros takes code 0
   (its elements are zero whatever the scale).
-* A block holding a NaN or an infinity takes the NaN scale (code 255): its
-  values, and every dot product that uses them, are NaN.  Its element codes are
-  ``encode(V_i)`` without scaling (NaN -> NaN code, +-inf -> +-max).
+* A block holding a NaN or an infinity takes the NaN scale (code 255) and the
+  NaN code 0x7F for every element: its values, and every dot product that uses
+  them, are NaN.
 * ``V_i / X`` is exact (a power-of-two division of an fp32 value, far from fp32
   overflow); a quotient below fp32's normal range encodes to zero either way.
 
@@ -88,7 +88,7 @@ def quantize_block(v: np.ndarray, fmt: int):
     v32 = np.asarray(v, dtype=np.float32)
     code = block_scale_code(oamax.amax(v32), fmt)
     if code == E8M0_NAN:
-        return encode(v32, fmt), code
+        return np.full(v32.shape, 0x7F, dtype=np.uint8), code
     q = np.ldexp(v32.astype(np.float64), -(code - E8M0_BIAS))
     with np.errstate(under="ignore"):
         return encode(q.astype(np.float32), fmt), code

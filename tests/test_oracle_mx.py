@@ -31,7 +31,10 @@ def _golden():
         c = np.zeros(32, np.uint8)
         for tok in codes.split():
             i, x = tok.split(":")
-            c[int(i)] = int(x, 16)
+            if i == "*":
+                c[:] = int(x, 16)
+            else:
+                c[int(i)] = int(x, 16)
         out.append((FMTS[f], v, int(sc, 16), c))
     return out
 
@@ -119,10 +122,10 @@ def test_degenerate_blocks():
     v = np.ones(32, np.float32)
     v[4] = np.inf
     c, s = omx.quantize_block(v, ofp8.E4M3)
-    assert s == 0xFF and c[4] == 0x7E and c[0] == 0x38
+    assert s == 0xFF and (c == 0x7F).all()
     v[4] = -np.nan
     c, s = omx.quantize_block(v, ofp8.E5M2)
-    assert s == 0xFF and (c[4] & 0x7F) == 0x7F
+    assert s == 0xFF and (c == 0x7F).all()
     d = omx.mx_dequant(c[None, :], np.array([[s]], np.uint8), ofp8.E5M2)
     assert np.isnan(d).all()
 
