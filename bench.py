@@ -247,8 +247,9 @@ def finer_report(torch, dsg, x, w, iters=10):
     """Finer-grained scaling on the benchmarked Linear's forward operands: the
     per-token cast of X [M x K] (a scale per row; 3 B/element, read once), the
     per-channel cast of W^T [N x K] (a scale per output channel), the per-tensor
-    current cast of X (amax pass, then the cast: 5 B/element) and the forward
-    GEMM with per-row x per-column dequant factors (2 M N K flop)."""
+    current cast of X (amax pass, then the cast: 5 B/element), the forward
+    GEMM with per-row x per-column dequant factors (2 M N K flop), and MXFP8:
+    the block casts of X and W^T and the MX forward GEMM."""
     print("[bench] finer scaling: per-token / per-channel / current", file=sys.stderr, flush=True)
     dev = x.device
     M, K = x.shape
@@ -288,7 +289,29 @@ def finer_report(torch, dsg, x, w, iters=10):
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     out["rowcol_gemm_fwd_nt"] = {"ms": round(ms, 4), "TFLOP/s": round(tflops, 1),
                                  "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4)}
-    del wt, xq, wq, y
+    # MXFP8: blocks of 32 along K with E8M0 scales (3 + 1/32 B per element cast)
+    xs = torch.empty(M, K // 32, dtype=torch.uint8, device=dev)
+    ws = torch.empty(N, K // 32, dtype=torch.uint8, device=dev)
+    for name, (fn, nbytes) in {
+            "mx_cast_x": (lambda: dsg.fp8ds_cast_mx(x, dsg.E4M3, xq, xs), (3 + 1 / 32) * M * K),
+            "mx_cast_wt": (lambda: dsg.fp8ds_cast_mx(wt, dsg.E4M3, wq, ws), (3 + 1 / 32) * N * K),
+    }.items():
+        fn()
+        ms = time_launches(torch, stream, fn, iters)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                     "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+
+    def mx_gemm():
+        dsg.fp8ds_gemm_mx(M, N, K, xq, dsg.E4M3, K, xs, K // 32, wq, dsg.E4M3, K, ws, K // 32, y, N,
+                          amax_y)
+
+    mx_gemm()
+    ms = time_launches(torch, stream, mx_gemm, iters)
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    out["mx_gemm_fwd_nt"] = {"ms": round(ms, 4), "TFLOP/s": round(tflops, 1),
+                             "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4)}
+    del wt, xq, wq, y, xs, ws
     torch.cuda.empty_cache()
     return out
 

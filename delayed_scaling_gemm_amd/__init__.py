@@ -73,6 +73,11 @@ def _declare(lib):
     lib.fp8ds_gemm_rowcol.restype = i32
     lib.fp8ds_gemm_rowcol.argtypes = [i32, i32, i64, i64, i64, vp, i32, i64, vp, vp, i32, i64, vp,
                                       vp, i32, i64, vp, vp]
+    lib.fp8ds_cast_mx.restype = i32
+    lib.fp8ds_cast_mx.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+    lib.fp8ds_gemm_mx.restype = i32
+    lib.fp8ds_gemm_mx.argtypes = [i64, i64, i64, vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, vp,
+                                  i32, i64, vp, vp]
     lib.fp8ds_gemm_batched.restype = i32
     lib.fp8ds_gemm_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i32, i64, i64, vp, vp, i32,
                                        i64, i64, vp, vp, i32, i64, i64, vp, i32, vp]
@@ -393,6 +398,39 @@ def fp8ds_gemm_rowcol(opa, opb, M, N, K, a, fa, lda, scale_inv_a, b, fb, ldb, sc
     _check(lib().fp8ds_gemm_rowcol(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_inv_a), _ptr(b),
                                    fb, ldb, _ptr(scale_inv_b), _ptr(c), _dtype_code(c), ldc,
                                    _ptr(amax_c), _stream(stream)))
+
+
+def fp8ds_cast_mx(x, fmt, q, scales, stream=None):
+    """MXFP8 cast of the 2-D ``x`` [rows, cols] (cols a multiple of 32) along its
+    rows: element codes into ``q`` (uint8 [rows, cols]) and one E8M0 code per
+    block of 32 into ``scales`` (uint8 [rows, cols / 32])."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    _need(x, "x", (torch.bfloat16, torch.float32), rows * cols)
+    _need(q, "q", (torch.uint8,), rows * cols)
+    _need(scales, "scales", (torch.uint8,), rows * cols // 32)
+    _check(lib().fp8ds_cast_mx(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(q), _ptr(scales),
+                               _stream(stream)))
+
+
+def fp8ds_gemm_mx(M, N, K, a, fa, lda, scales_a, ld_scales_a, b, fb, ldb, scales_b, ld_scales_b,
+                  c, ldc, amax_c=None, stream=None):
+    """MXFP8 GEMM ``C = A B^T``: A [M, K] and B [N, K] element codes with E8M0
+    block scales [M, ld_scales_a] / [N, ld_scales_b] along K; K a multiple of 128."""
+    import torch
+
+    for t, name, n in ((a, "a", _span(M, K, lda)), (b, "b", _span(N, K, ldb)),
+                       (scales_a, "scales_a", _span(M, K // 32, ld_scales_a)),
+                       (scales_b, "scales_b", _span(N, K // 32, ld_scales_b))):
+        _need(t, name, (torch.uint8,), n, contiguous=False)
+    _need(c, "c", (torch.bfloat16, torch.float32), _span(M, N, ldc), contiguous=False)
+    _need(amax_c, "amax_c", (torch.float32,), 1)
+    _check(lib().fp8ds_gemm_mx(M, N, K, _ptr(a), fa, lda, _ptr(scales_a), ld_scales_a, _ptr(b), fb,
+                               ldb, _ptr(scales_b), ld_scales_b, _ptr(c), _dtype_code(c), ldc,
+                               _ptr(amax_c), _stream(stream)))
 
 
 def abi_version() -> int:

@@ -407,3 +407,77 @@ int fp8ds_cast_current(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int fp8ds_cast_mx(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+                  uint8_t* q, uint8_t* scales, hipStream_t stream) {
+  const char* who = "fp8ds_cast_mx";
+  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "%s: bad dtype %d", who, (int)xt);
+  if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "%s: bad format %d", who, (int)fmt);
+  if (rows < 0 || cols < 0 || (cols > 0 && rows > kMaxElems / cols))
+    return fail(FP8DS_ERR_SHAPE, "%s: bad shape %lld x %lld", who, (long long)rows,
+                (long long)cols);
+  if (cols % 32 != 0)
+    return fail(FP8DS_ERR_SHAPE, "%s: the row length %lld is not a multiple of the block (32)",
+                who, (long long)cols);
+  const int64_t n = rows * cols;
+  if (n == 0) return ok();
+  if (!x || !q || !scales) return fail(FP8DS_ERR_NULL, "%s: x, q and scales are required", who);
+  if (!aligned16(x) || !aligned16(q))
+    return fail(FP8DS_ERR_ALIGN, "%s: x and q must be 16-byte aligned", who);
+  return hip_status(fp8ds::launch_mx_cast(x, xt == FP8DS_BF16, n, (int)fmt, q, scales, stream),
+                    who);
+}
+
+int fp8ds_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* A, fp8ds_format fa, int64_t lda,
+                  const uint8_t* scales_a, int64_t ld_scales_a, const uint8_t* B, fp8ds_format fb,
+                  int64_t ldb, const uint8_t* scales_b, int64_t ld_scales_b, void* C,
+                  fp8ds_dtype ct, int64_t ldc, float* amax_c, hipStream_t stream) {
+  const char* who = "fp8ds_gemm_mx";
+  if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8DS_ERR_ENUM, "%s: bad format", who);
+  if (!valid_dtype(ct)) return fail(FP8DS_ERR_ENUM, "%s: bad output dtype", who);
+  const int64_t lim = int64_t(1) << 31;
+  if (M < 0 || N < 0 || K < 0 || M >= lim || N >= lim || K >= lim)
+    return fail(FP8DS_ERR_SHAPE, "%s: bad M/N/K %lld/%lld/%lld", who, (long long)M, (long long)N,
+                (long long)K);
+  if (K % 128 != 0)
+    return fail(FP8DS_ERR_SHAPE, "%s: K = %lld is not a multiple of 128", who, (long long)K);
+  if (((M + 127) / 128) * ((N + 127) / 128) >= lim)
+    return fail(FP8DS_ERR_SHAPE, "%s: M x N %lld x %lld has too many tiles", who, (long long)M,
+                (long long)N);
+  if (M == 0 || N == 0) {
+    if (amax_c)
+      return hip_status(fp8ds::launch_prologue(1, nullptr, nullptr, amax_c, nullptr, stream), who);
+    return ok();
+  }
+  if (lda < K || ldb < K || ldc < N || ld_scales_a < K / 32 || ld_scales_b < K / 32)
+    return fail(FP8DS_ERR_SHAPE, "%s: leading dimension too small", who);
+  if (!C || (K > 0 && (!A || !B || !scales_a || !scales_b)))
+    return fail(FP8DS_ERR_NULL, "%s: A, B, their scales and C are required", who);
+  const int esz = ct == FP8DS_BF16 ? 2 : 4;
+  if ((K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16)) || !aligned16(C) ||
+      (ldc * esz) % 16)
+    return fail(FP8DS_ERR_ALIGN, "%s: A, B, C and lda, ldb, ldc*elem_size must be 16-byte aligned",
+                who);
+  if (K > 0 && ((reinterpret_cast<uintptr_t>(scales_a) & 3u) ||
+                (reinterpret_cast<uintptr_t>(scales_b) & 3u) || ld_scales_a % 4 || ld_scales_b % 4))
+    return fail(FP8DS_ERR_ALIGN, "%s: the scale arrays and their leading dimensions must be "
+                "4-byte aligned", who);
+  hipError_t e = hipSuccess;
+  if (amax_c) e = fp8ds::launch_prologue(1, nullptr, nullptr, amax_c, nullptr, stream);
+  if (e == hipSuccess) {
+    fp8ds::GemmProblem p;
+    p.opa = 0; p.opb = 1;
+    p.M = M; p.N = N; p.K = K;
+    p.A = A; p.fa = (int)fa; p.lda = lda; p.scale_a = nullptr;
+    p.B = B; p.fb = (int)fb; p.ldb = ldb; p.scale_b = nullptr;
+    p.C = C; p.out_bf16 = ct == FP8DS_BF16; p.ldc = ldc; p.amax_c = amax_c;
+    p.batch = 1; p.stride_a = 0; p.stride_b = 0; p.stride_c = 0;
+    p.sc_a = scales_a; p.sc_b = scales_b; p.ldsa = ld_scales_a; p.ldsb = ld_scales_b;
+    e = fp8ds::launch_gemm_mx(p, num_cus(), stream);
+  }
+  return hip_status(e, who);
+}
+
+}  // extern "C"

@@ -49,6 +49,41 @@ __device__ __forceinline__ uint32_t encode4_hw(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
+// ------------------------------------------------------------------ 16-byte pieces
+// A piece is 16 bytes of input: 8 BF16 or 4 FP32 elements.
+
+// The largest |x| bit pattern of one 16-byte piece.
+template <bool BF16>
+__device__ __forceinline__ uint32_t piece_amax(const u32x4& d) {
+  if constexpr (BF16) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max((d[k] & 0x7FFFu) << 16, d[k] & 0x7FFF0000u));
+    return m;
+  } else {
+    return max(max(d.x & 0x7FFFFFFFu, d.y & 0x7FFFFFFFu), max(d.z & 0x7FFFFFFFu, d.w & 0x7FFFFFFFu));
+  }
+}
+
+// Four codes of four scaled values (software encoder if any is NaN).
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+  const bool nan = a != a || b != b || c != c || d != d;
+  return nan ? encode4_sw<FMT>(a, b, c, d) : encode4_hw<FMT>(a, b, c, d);
+}
+
+// Codes of one piece: 8 bytes (BF16, returned in .x/.y) or 4 bytes (FP32, in .x).
+template <bool BF16, int FMT>
+__device__ __forceinline__ u32x2 piece_codes(const u32x4& d, float s) {
+  if constexpr (BF16) {
+    return u32x2{encode4<FMT>(bf16_lo(d.x) * s, bf16_hi(d.x) * s, bf16_lo(d.y) * s, bf16_hi(d.y) * s),
+                 encode4<FMT>(bf16_lo(d.z) * s, bf16_hi(d.z) * s, bf16_lo(d.w) * s, bf16_hi(d.w) * s)};
+  } else {
+    return u32x2{encode4<FMT>(__uint_as_float(d.x) * s, __uint_as_float(d.y) * s,
+                              __uint_as_float(d.z) * s, __uint_as_float(d.w) * s), 0u};
+  }
+}
+
 template <int FMT>
 __device__ __forceinline__ uint32_t sat4(float a, float b, float c, float d) {
   constexpr float M = FmtTraits<FMT>::kMax;

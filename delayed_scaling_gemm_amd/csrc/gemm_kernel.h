@@ -54,6 +54,7 @@ namespace fp8ds {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -75,6 +76,9 @@ struct GemmArgs {
   int out_f32;
   const float* inv_a;  // VS: inverse scale per row of op(A) [M]
   const float* inv_b;  // VS: inverse scale per column of op(B) [N]
+  const uint8_t* sc_a;  // MX: E8M0 scale of each 32-element block of a row of A [M][ldsa]
+  const uint8_t* sc_b;  // MX: the same for B [N][ldsb]
+  int64_t ldsa, ldsb;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 4)) & 7; }
@@ -119,6 +123,27 @@ __device__ __forceinline__ uint32_t widen_pair(uint32_t d, bool hi) {
     // selector bytes: 0x0C = constant 0x00; 0x00..0x03 = bytes of d
     return __builtin_amdgcn_perm(0u, d, hi ? 0x030C020Cu : 0x010C000Cu);
   }
+}
+
+// MX: two FP8 bytes -> two BF16 values times the block's power-of-two scale s
+// (V_CVT_SCALEF32_PK_BF16_FP8 / _BF8).  BF16 has the exponent range of fp32 and
+// 8 significant bits, so decode(byte) * s is exact while it stays a normal BF16
+// number; a NaN byte stays NaN.
+template <int FMT>
+__device__ __forceinline__ uint32_t widen_pair_mx(uint32_t d, bool hi, float s) {
+  if constexpr (FMT == kE4M3) {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, s, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, s, false));
+  } else {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d, s, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d, s, false));
+  }
+}
+
+// The value 2^(code - 127) of an E8M0 scale code (2^128 = inf for the NaN code
+// 255, whose blocks hold NaN bytes only).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+  return __builtin_amdgcn_ldexpf(1.0f, (int)code - 127);
 }
 
 // 16 FP8 bytes -> 16 F16 as two 16-byte groups (bytes 0..7, bytes 8..15).
@@ -565,8 +590,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
 // FP8: a stage is 2 MFMA steps of K = 64 (32x32x64 F8F6F4), each on two chunks.
 
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT,
-          bool VS = false>
+          bool VS = false, bool MX = false>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
+  static_assert(!MX || (EXACT && DIRECT && A_KC && B_KC && !VS),
+                "MX blocks run along K: both operands K-contiguous, direct loads, exact path");
   constexpr int NT = 256;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -601,7 +628,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 
   const int nk = (int)((K + KB - 1) / KB);
   // dequant factor (VS: the per-row / per-column factors are applied in the epilogue)
-  const float d = VS ? 1.0f : __fdiv_rn(1.0f, p.scale_a[bz] * p.scale_b[bz]);
+  const float d = (VS || MX) ? 1.0f : __fdiv_rn(1.0f, p.scale_a[bz] * p.scale_b[bz]);
   const int fr = lane & 31;
   const int fc = (lane >> 5) * 4;  // first of this lane's four chunks
 
@@ -657,20 +684,68 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     u32x4 ra[2][FM], rb[2][FN];      // raw chunks, by unit parity
     u32x2 ha[2][FM][2], hb[2][FN][2]; // F16 operands of a step (8 values = 2 x u32x2), by step parity
 
-    // widen one half (8 bytes) of every raw chunk of a unit into F16 set `dst`
+    // MX: the E8M0 scales of this lane's rows, 4 blocks (one stage of 128 K) per
+    // dword.  A unit u of a stage covers K bytes [64 (lane / 32) + 16 u, + 16),
+    // i.e. block 2 (lane / 32) + u / 2 of the stage.  `sc*_nxt` holds the running
+    // stage's dwords until its second half has taken them (step 3), then the next
+    // stage's, loaded there; `sf*` the scale values of the running half stage.
+    uint32_t sca_nxt[FM], scb_nxt[FN];
+    float sfa[FM], sfb[FN];
+    const int sc_shift = 16 * (lane >> 5);
+    auto load_scales = [&](int kt) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int64_t r = min(m0 + wm * WTM + i * 32 + fr, M - 1);
+          sca_nxt[i] = *reinterpret_cast<const uint32_t*>(p.sc_a + r * p.ldsa + 4 * (int64_t)kt);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t r = min(n0 + wn * WTN + j * 32 + fr, N - 1);
+          scb_nxt[j] = *reinterpret_cast<const uint32_t*>(p.sc_b + r * p.ldsb + 4 * (int64_t)kt);
+        }
+      }
+    };
+    auto scale_f = [&](uint32_t dw, int hb2) {
+      return e8m0_to_f32(__builtin_amdgcn_ubfe(dw, sc_shift + 8 * hb2, 8));
+    };
+    auto take_scales = [&](int hb2) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) sfa[i] = scale_f(sca_nxt[i], hb2);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sfb[j] = scale_f(scb_nxt[j], hb2);
+      }
+    };
+
+    // widen one half (8 bytes) of every raw chunk of a unit into F16 (MX: scaled
+    // BF16) set `dst`; `u` is the unit within its stage, `next`: the unit belongs
+    // to the stage after the running one (MX scales not taken yet)
     auto widen_step = [&](const u32x4 (&xa)[FM], const u32x4 (&xb)[FN], int half,
-                          u32x2 (&da)[FM][2], u32x2 (&db)[FN][2]) {
+                          u32x2 (&da)[FM][2], u32x2 (&db)[FN][2], int u, bool next) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const uint32_t w0 = xb[j][2 * half], w1 = xb[j][2 * half + 1];
-        db[j][0] = u32x2{widen_pair<FB>(w0, false), widen_pair<FB>(w0, true)};
-        db[j][1] = u32x2{widen_pair<FB>(w1, false), widen_pair<FB>(w1, true)};
+        if constexpr (MX) {
+          const float s = next ? scale_f(scb_nxt[j], 0) : sfb[j];
+          db[j][0] = u32x2{widen_pair_mx<FB>(w0, false, s), widen_pair_mx<FB>(w0, true, s)};
+          db[j][1] = u32x2{widen_pair_mx<FB>(w1, false, s), widen_pair_mx<FB>(w1, true, s)};
+        } else {
+          db[j][0] = u32x2{widen_pair<FB>(w0, false), widen_pair<FB>(w0, true)};
+          db[j][1] = u32x2{widen_pair<FB>(w1, false), widen_pair<FB>(w1, true)};
+        }
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint32_t w0 = xa[i][2 * half], w1 = xa[i][2 * half + 1];
-        da[i][0] = u32x2{widen_pair<FA>(w0, false), widen_pair<FA>(w0, true)};
-        da[i][1] = u32x2{widen_pair<FA>(w1, false), widen_pair<FA>(w1, true)};
+        if constexpr (MX) {
+          const float s = next ? scale_f(sca_nxt[i], 0) : sfa[i];
+          da[i][0] = u32x2{widen_pair_mx<FA>(w0, false, s), widen_pair_mx<FA>(w0, true, s)};
+          da[i][1] = u32x2{widen_pair_mx<FA>(w1, false, s), widen_pair_mx<FA>(w1, true, s)};
+        } else {
+          da[i][0] = u32x2{widen_pair<FA>(w0, false), widen_pair<FA>(w0, true)};
+          da[i][1] = u32x2{widen_pair<FA>(w1, false), widen_pair<FA>(w1, true)};
+        }
       }
     };
     auto mma = [&](const u32x2 (&da)[FM][2], const u32x2 (&db)[FN][2]) {
@@ -682,13 +757,18 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
           const v8h bv =
               __builtin_bit_cast(v8h, u32x4{db[j][0][0], db[j][0][1], db[j][1][0], db[j][1][1]});
           // first operand = B block, second = A block: the result is the C^T block
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, av, acc[i][j], 0, 0, 0);
+          if constexpr (MX)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(v8bf, bv), __builtin_bit_cast(v8bf, av), acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, av, acc[i][j], 0, 0, 0);
         }
       }
     };
 
     if (nk > 0) {
       if constexpr (DIRECT) {
+        load_scales(0);
         issue_direct(0, 0);
         if (nk > 1) issue_direct(1, 1);
         vmem_wait_all();
@@ -700,12 +780,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       }
       __syncthreads();
       read_unit(0, 0, ra[0], rb[0]);
-      widen_step(ra[0], rb[0], 0, ha[0], hb[0]);
+      widen_step(ra[0], rb[0], 0, ha[0], hb[0], 0, true);
     }
 
     auto stage = [&](int kt, auto more_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
       const int cur = kt & 1;
+      if constexpr (MX) take_scales(0);  // units 0, 1 of this stage (loaded a stage ago)
       if constexpr (MORE && !DIRECT) {
         la.load(A, p.lda, m0, M, (int64_t)(kt + 1) * KB, K, tid);
         lb.load(B, p.ldb, n0, N, (int64_t)(kt + 1) * KB, K, tid);
@@ -730,12 +811,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
             }
           }
         }
+        if constexpr (MX) {
+          if (t == 3) {
+            take_scales(1);  // units 2, 3: widened from step 3 on
+            if constexpr (MORE) load_scales(kt + 1);
+          }
+        }
         // widen the operands of step t + 1 (the next stage's step 0 after t = 7)
         if (t < 7) {
           const int un = (t + 1) >> 1;
-          widen_step(ra[un & 1], rb[un & 1], (t + 1) & 1, ha[(t + 1) & 1], hb[(t + 1) & 1]);
+          widen_step(ra[un & 1], rb[un & 1], (t + 1) & 1, ha[(t + 1) & 1], hb[(t + 1) & 1], un,
+                     false);
         } else if constexpr (MORE) {
-          widen_step(ra[0], rb[0], 0, ha[0], hb[0]);
+          widen_step(ra[0], rb[0], 0, ha[0], hb[0], 0, true);
         }
         mma(ha[t & 1], hb[t & 1]);
         // keep each step's reads, stores and widening inside the step they were
@@ -846,7 +934,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 
 // ------------------------------------------------------------------ dispatch
 
-template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT, bool VS>
+template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT, bool VS,
+          bool MX = false>
 static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   GemmArgs a;
   a.M = q.M; a.N = q.N; a.K = q.K;
@@ -859,9 +948,11 @@ static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   a.out_f32 = q.out_bf16 ? 0 : 1;
   a.inv_a = q.inv_a;
   a.inv_b = q.inv_b;
+  a.sc_a = q.sc_a; a.sc_b = q.sc_b;
+  a.ldsa = q.ldsa; a.ldsb = q.ldsb;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)q.batch);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, EXACT, DIRECT, VS>), grid, dim3(256),
-                     0, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, EXACT, DIRECT, VS, MX>), grid,
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

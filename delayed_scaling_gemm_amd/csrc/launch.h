@@ -91,6 +91,9 @@ struct GemmProblem {
   int64_t stride_a, stride_b, stride_c;  // bytes, bytes, elements
   const float* inv_a = nullptr;  // scale vectors (launch_gemm_rowcol): [M], [N]
   const float* inv_b = nullptr;
+  const uint8_t* sc_a = nullptr;  // MX block scales (launch_gemm_mx): [M][ldsa], [N][ldsb]
+  const uint8_t* sc_b = nullptr;
+  int64_t ldsa = 0, ldsb = 0;
 };
 // EXACT datapath: FP8 widened to F16, F16 MFMA, FP32 sums.
 hipError_t launch_gemm_exact(const GemmProblem& p, int num_cus, hipStream_t stream);
@@ -99,5 +102,13 @@ hipError_t launch_gemm_fp8(const GemmProblem& p, int num_cus, hipStream_t stream
 // EXACT datapath with one inverse scale per row of op(A) and per column of op(B)
 // (p.inv_a, p.inv_b; batch 1).
 hipError_t launch_gemm_rowcol(const GemmProblem& p, int num_cus, hipStream_t stream);
+// MXFP8 GEMM C = A B^T (opa N, opb T), A and B blocked along K with E8M0 scales
+// p.sc_a / p.sc_b; K a multiple of 128, operands 16-byte aligned, batch 1.
+// EXACT datapath with the scales folded into the BF16 widening.
+hipError_t launch_gemm_mx(const GemmProblem& p, int num_cus, hipStream_t stream);
+
+// MXFP8 cast of n elements (blocks of 32 consecutive elements): q [n], scales [n / 32].
+hipError_t launch_mx_cast(const void* x, bool bf16, int64_t n, int fmt, uint8_t* q,
+                          uint8_t* scales, hipStream_t stream);
 
 }  // namespace fp8ds

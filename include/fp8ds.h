@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FP8DS_ABI_VERSION 5
+#define FP8DS_ABI_VERSION 6
 
 typedef enum {
   FP8DS_OK = 0,
@@ -372,6 +372,58 @@ int fp8ds_gemm_rowcol(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t 
                       const uint8_t* A, fp8ds_format fa, int64_t lda, const float* scale_inv_a,
                       const uint8_t* B, fp8ds_format fb, int64_t ldb, const float* scale_inv_b,
                       void* C, fp8ds_dtype ct, int64_t ldc, float* amax_c, hipStream_t stream);
+
+/*
+ * MXFP8: FP8 elements in blocks of 32 consecutive elements along a row (the
+ * contraction dimension of the GEMM below), each block with one E8M0 scale.
+ * [P2] §九 "展望：Blackwell 的 Microscaling 与未来" (32 FP8 values share an 8-bit
+ * E8M0 scale, scaled block by block); the block rule, which that figure leaves
+ * garbled, is the OCP Microscaling Formats (MX) specification's:
+ *   a = max |x_i| over the block;   E8M0 code = floor(log2 a) - emax + 127,
+ *   clamped to [0, 254] (emax = 8 for E4M3, 15 for E5M2; a zero block has code 0);
+ *   q_i = encode(x_i / 2^(code - 127)), saturating round-to-nearest-even.
+ * A block holding a NaN or an infinity gets code 255 (NaN) and the element code
+ * 0x7F (NaN) throughout.  The value of element i is 2^(code - 127) * decode(q_i).
+ */
+
+/*
+ * fp8ds_cast_mx -- MXFP8 quantization of a [rows x cols] matrix along its rows.
+ *
+ *   x        device, rows*cols elements of `xt`, row-major, 16-byte aligned.
+ *   cols     a multiple of 32 (else FP8DS_ERR_SHAPE).
+ *   q        device, rows*cols bytes, 16-byte aligned: the element codes.
+ *   scales   device, rows*cols/32 bytes: the E8M0 code of block b of row r at
+ *            [r * cols/32 + b].
+ * A column-blocked copy (blocks along the other dimension) is this call on the
+ * transposed matrix.  No amax, scale state or history is involved.
+ */
+int fp8ds_cast_mx(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+                  uint8_t* q, uint8_t* scales, hipStream_t stream);
+
+/*
+ * fp8ds_gemm_mx -- MXFP8 GEMM  C = A B^T  with FP32 accumulation:
+ *   C[i][j] = convert_ct( sum_k X_a(i, k/32) a(i,k) X_b(j, k/32) b(j,k) )
+ * with a, b the decoded element codes and X the block scales.  Exact datapath:
+ * every element is widened to BF16 times its block scale (exact while the scaled
+ * value is a normal BF16 number, i.e. |X * decode| >= 2^-126, or zero: blocks whose
+ * scale code is above about 17) and multiplied on the BF16 matrix cores with
+ * FP32 sums; a NaN block makes every output it touches NaN.
+ *
+ *   A          device [M x K] codes (K-contiguous, leading dimension lda), format fa.
+ *   scales_a   device [M x ld_scales_a] E8M0 codes; block b of row i at
+ *              [i * ld_scales_a + b] (fp8ds_cast_mx of A writes ld = K/32).
+ *   B          device [N x K] codes (leading dimension ldb), format fb; for a
+ *              Linear Y = X W with W [K x N], B is the MX cast of W^T.
+ *   scales_b   device [N x ld_scales_b] E8M0 codes.
+ *   C          device [M x ldc], BF16 or FP32 (ct).   amax_c  device or NULL: max |C|.
+ *   K          a multiple of 128 (four blocks per pipeline stage), else FP8DS_ERR_SHAPE.
+ *   A, B, C, lda, ldb, ldc * element size: 16-byte aligned; the scale arrays and
+ *   ld_scales_a / ld_scales_b: 4-byte aligned (FP8DS_ERR_ALIGN otherwise).
+ */
+int fp8ds_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* A, fp8ds_format fa, int64_t lda,
+                  const uint8_t* scales_a, int64_t ld_scales_a, const uint8_t* B, fp8ds_format fb,
+                  int64_t ldb, const uint8_t* scales_b, int64_t ld_scales_b, void* C,
+                  fp8ds_dtype ct, int64_t ldc, float* amax_c, hipStream_t stream);
 
 #ifdef __cplusplus
 }

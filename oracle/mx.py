@@ -97,17 +97,29 @@ def quantize_block(v: np.ndarray, fmt: int):
 def mx_cast(x: np.ndarray, fmt: int):
     """MX-quantize a 2-D array along its rows (blocks of 32 consecutive elements
     of a row; the row length must be a multiple of 32).  Returns ``(codes [R, C]
-    uint8, scales [R, C/32] uint8)``."""
+    uint8, scales [R, C/32] uint8)``.
+
+    The same steps as :func:`quantize_block`, taken for all blocks at once with
+    array operations (the tests check the two against each other)."""
     x32 = np.asarray(x, dtype=np.float32)
     R, C = x32.shape
     assert C % BLOCK == 0, "row length must be a multiple of 32"
-    codes = np.zeros((R, C), dtype=np.uint8)
-    scales = np.zeros((R, C // BLOCK), dtype=np.uint8)
-    for r in range(R):
-        for b in range(C // BLOCK):
-            c, s = quantize_block(x32[r, BLOCK * b:BLOCK * (b + 1)], fmt)
-            codes[r, BLOCK * b:BLOCK * (b + 1)] = c
-            scales[r, b] = s
+    blocks = x32.reshape(R, C // BLOCK, BLOCK).astype(np.float64)
+    special = ~np.isfinite(blocks).all(axis=-1)              # NaN or Inf in the block
+    amax = np.where(special[..., None], 0.0, np.abs(blocks)).max(axis=-1)
+    _, e = np.frexp(amax)                                     # amax = m * 2**e, 0.5 <= m < 1
+    E = np.clip(e.astype(np.int64) - 1 - EMAX_ELEM[fmt], -E8M0_BIAS, E8M0_BIAS)
+    scales = np.where(amax == 0.0, 0, E + E8M0_BIAS)
+    scales = np.where(special, E8M0_NAN, scales).astype(np.uint8)
+    shift = np.where(special, 0, scales.astype(np.int64) - E8M0_BIAS)
+    q = np.ldexp(np.where(special[..., None], 0.0, blocks), -shift[..., None])
+    q32 = q.astype(np.float32).ravel()
+    codes = np.empty(q32.size, dtype=np.uint8)
+    step = 1 << 20  # elementwise: encoded in pieces to keep numpy's temporaries small
+    for i in range(0, q32.size, step):
+        codes[i:i + step] = encode(q32[i:i + step], fmt)
+    codes = codes.reshape(R, C)
+    codes = np.where(np.repeat(special, BLOCK, axis=1), np.uint8(0x7F), codes).astype(np.uint8)
     return codes, scales
 
 

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8ds_amax", "fp8ds_cast", "fp8ds_cast_batched", "fp8ds_scale_update",
               "fp8ds_gemm", "fp8ds_gemm_batched", "fp8ds_status_string", "fp8ds_last_error",
-              "fp8ds_abi_version", "fp8ds_adamw", "fp8ds_cast_health"):
+              "fp8ds_abi_version", "fp8ds_adamw", "fp8ds_cast_health", "fp8ds_cast_rowwise",
+              "fp8ds_cast_current", "fp8ds_gemm_rowcol", "fp8ds_cast_mx", "fp8ds_gemm_mx"):
         assert n in names
 
 
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(dsg.LIB_PATH)
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert dsg.abi_version() == 5
+    assert dsg.abi_version() == 6
 
 
 def test_status_strings():
@@ -145,3 +146,27 @@ def test_finer_scaling_validation_errors_without_gpu():
     assert g(1, 1) == -6
     assert g(0, 1, sb=p + 4) == -4
     assert g(0, 1, sa=None) == -1
+
+
+def test_mx_validation_errors_without_gpu():
+    L = dsg.lib()
+    p = 0x1000
+    # fp8ds_cast_mx(x, xt, rows, cols, fmt, q, scales, stream)
+    assert L.fp8ds_cast_mx(p, 1, 4, 48, 0, p, p, None) == -2     # cols not a multiple of 32
+    assert L.fp8ds_cast_mx(p, 1, 4, 64, 5, p, p, None) == -3     # bad format
+    assert L.fp8ds_cast_mx(p, 9, 4, 64, 0, p, p, None) == -3     # bad dtype
+    assert L.fp8ds_cast_mx(p, 1, 4, 64, 0, p, None, None) == -1  # scales missing
+    assert L.fp8ds_cast_mx(p + 8, 1, 4, 64, 0, p, p, None) == -4
+    assert L.fp8ds_cast_mx(p, 1, 0, 64, 0, None, None, None) == 0  # empty: no-op
+    # fp8ds_gemm_mx(M, N, K, A, fa, lda, sa, ldsa, B, fb, ldb, sb, ldsb, C, ct, ldc, amax, s)
+    g = lambda K=256, lda=256, sa=p, ldsa=8, sb=p, C=p: L.fp8ds_gemm_mx(
+        64, 64, K, p, 0, lda, sa, ldsa, p, 1, 256, sb, 8, C, 1, 64, None, None)
+    assert g(K=192, lda=192) == -2   # K not a multiple of 128
+    assert g(lda=128) == -2          # lda < K
+    assert g(ldsa=4) == -2           # scale leading dimension < K / 32
+    assert g(sa=None) == -1
+    assert g(C=None) == -1
+    assert g(sb=p + 2) == -4         # scale array not 4-byte aligned
+    assert g(ldsa=10) == -4          # scale leading dimension not a multiple of 4
+    assert L.fp8ds_gemm_mx(64, 64, 256, p, 7, 256, p, 8, p, 0, 256, p, 8, p, 1, 64, None,
+                           None) == -3

@@ -162,3 +162,20 @@ def test_gemm_brute_force_fractions():
                 tot += (fa[a[i, k]] * Fraction(2) ** (int(sa[i, k // 32]) - 127) *
                         fb[b[j, k]] * Fraction(2) ** (int(sb[j, k // 32]) - 127))
             assert abs(Fraction(acc[i, j]) - tot) <= abs(tot) * Fraction(1, 2**50) + Fraction(1, 2**200)
+
+
+@pytest.mark.parametrize("fmt", [ofp8.E4M3, ofp8.E5M2])
+def test_array_cast_equals_blockwise_definition(fmt):
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((9, 256)) *
+         np.repeat(2.0 ** rng.integers(-140, 120, (9, 8)), 32, axis=1)).astype(np.float32)
+    x[0, :32] = 0.0
+    x[1, 40] = np.inf
+    x[2, 70] = -np.nan
+    x[3, 100] = np.float32(1.9 * 2**7)
+    codes, scales = omx.mx_cast(x, fmt)
+    for r in range(9):
+        for b in range(8):
+            c, s = omx.quantize_block(x[r, 32 * b:32 * (b + 1)], fmt)
+            assert scales[r, b] == s
+            np.testing.assert_array_equal(codes[r, 32 * b:32 * (b + 1)], c)
