@@ -74,7 +74,7 @@ def _declare(lib):
     lib.fp8ds_gemm_rowcol.argtypes = [i32, i32, i64, i64, i64, vp, i32, i64, vp, vp, i32, i64, vp,
                                       vp, i32, i64, vp, vp]
     lib.fp8ds_cast_mx.restype = i32
-    lib.fp8ds_cast_mx.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+    lib.fp8ds_cast_mx.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.fp8ds_gemm_mx.restype = i32
     lib.fp8ds_gemm_mx.argtypes = [i64, i64, i64, vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, vp,
                                   i32, i64, vp, vp]
@@ -400,10 +400,12 @@ def fp8ds_gemm_rowcol(opa, opb, M, N, K, a, fa, lda, scale_inv_a, b, fb, ldb, sc
                                    _ptr(amax_c), _stream(stream)))
 
 
-def fp8ds_cast_mx(x, fmt, q, scales, stream=None):
+def fp8ds_cast_mx(x, fmt, q, scales, q_t=None, scales_t=None, stream=None):
     """MXFP8 cast of the 2-D ``x`` [rows, cols] (cols a multiple of 32) along its
     rows: element codes into ``q`` (uint8 [rows, cols]) and one E8M0 code per
-    block of 32 into ``scales`` (uint8 [rows, cols / 32])."""
+    block of 32 into ``scales`` (uint8 [rows, cols / 32]); optionally the
+    transpose blocked along its own rows into ``q_t`` [cols, rows] and
+    ``scales_t`` [cols, rows / 32] (rows and cols multiples of 128)."""
     import torch
 
     if x.dim() != 2:
@@ -412,8 +414,10 @@ def fp8ds_cast_mx(x, fmt, q, scales, stream=None):
     _need(x, "x", (torch.bfloat16, torch.float32), rows * cols)
     _need(q, "q", (torch.uint8,), rows * cols)
     _need(scales, "scales", (torch.uint8,), rows * cols // 32)
+    _need(q_t, "q_t", (torch.uint8,), rows * cols)
+    _need(scales_t, "scales_t", (torch.uint8,), rows * cols // 32)
     _check(lib().fp8ds_cast_mx(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(q), _ptr(scales),
-                               _stream(stream)))
+                               _ptr(q_t), _ptr(scales_t), _stream(stream)))
 
 
 def fp8ds_gemm_mx(M, N, K, a, fa, lda, scales_a, ld_scales_a, b, fb, ldb, scales_b, ld_scales_b,

@@ -411,7 +411,8 @@ int fp8ds_cast_current(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols
 extern "C" {
 
 int fp8ds_cast_mx(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
-                  uint8_t* q, uint8_t* scales, hipStream_t stream) {
+                  uint8_t* q, uint8_t* scales, uint8_t* q_t, uint8_t* scales_t,
+                  hipStream_t stream) {
   const char* who = "fp8ds_cast_mx";
   if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "%s: bad dtype %d", who, (int)xt);
   if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "%s: bad format %d", who, (int)fmt);
@@ -426,6 +427,19 @@ int fp8ds_cast_mx(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8
   if (!x || !q || !scales) return fail(FP8DS_ERR_NULL, "%s: x, q and scales are required", who);
   if (!aligned16(x) || !aligned16(q))
     return fail(FP8DS_ERR_ALIGN, "%s: x and q must be 16-byte aligned", who);
+  if (!q_t != !scales_t)
+    return fail(FP8DS_ERR_NULL, "%s: q_t and scales_t go together", who);
+  if (q_t) {
+    if (rows % 128 || cols % 128)
+      return fail(FP8DS_ERR_SHAPE, "%s: a transposed copy needs rows and cols in multiples of "
+                  "128 (got %lld x %lld)", who, (long long)rows, (long long)cols);
+    if (rows / 128 > 65535 || cols / 128 > (int64_t(1) << 31) - 1)
+      return fail(FP8DS_ERR_SHAPE, "%s: too many 128-row tiles for a transposed copy", who);
+    if (!aligned16(q_t)) return fail(FP8DS_ERR_ALIGN, "%s: q_t must be 16-byte aligned", who);
+    return hip_status(fp8ds::launch_mx_cast_transpose(x, xt == FP8DS_BF16, rows, cols, (int)fmt,
+                                                      q, scales, q_t, scales_t, stream),
+                      who);
+  }
   return hip_status(fp8ds::launch_mx_cast(x, xt == FP8DS_BF16, n, (int)fmt, q, scales, stream),
                     who);
 }

@@ -110,5 +110,10 @@ hipError_t launch_gemm_mx(const GemmProblem& p, int num_cus, hipStream_t stream)
 // MXFP8 cast of n elements (blocks of 32 consecutive elements): q [n], scales [n / 32].
 hipError_t launch_mx_cast(const void* x, bool bf16, int64_t n, int fmt, uint8_t* q,
                           uint8_t* scales, hipStream_t stream);
+// The same of a [rows x cols] matrix (both multiples of 128) plus its transpose q_t
+// [cols x rows] blocked along its own rows, scales_t [cols][rows / 32].
+hipError_t launch_mx_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
+                                    uint8_t* q, uint8_t* scales, uint8_t* qt, uint8_t* scales_t,
+                                    hipStream_t stream);
 
 }  // namespace fp8ds

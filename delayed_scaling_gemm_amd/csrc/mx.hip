@@ -74,6 +74,178 @@ __global__ __launch_bounds__(256) void mx_cast_kernel(const void* __restrict__ x
   }
 }
 
+// ------------------------------------------------------------------ both orientations
+// One read of x, two MX copies: q [rows x cols] with blocks along rows (as
+// mx_cast_kernel) and q_t [cols x rows] = the transpose with blocks of 32
+// consecutive rows of each column, i.e. blocks along the rows of q_t, with
+// scales_t [cols][rows / 32].  A 128 x 128 tile per 256-thread workgroup (the
+// layout of cast_transpose_kernel): pass i holds rows 32 i .. 32 i + 31 of the
+// tile -- exactly one column block -- as lane-contiguous 16-byte pieces, every
+// piece of a thread in the same 8 (BF16) or 4 (FP32) columns.  Row blocks are
+// reduced by lane shuffles as in mx_cast_kernel; a column block's amax is the
+// max over the thread's own pieces, then over the lanes of the same columns
+// (shuffles), then over the four waves through LDS.  Column codes are parked in
+// an LDS tile and written transposed by tile_store_qt.  Whole tiles only.
+
+// Codes of one piece with one multiplier per element (column); columns whose
+// block holds NaN or Inf (code 255) get the NaN code.
+template <bool BF16, int FMT>
+__device__ __forceinline__ u32x2 piece_codes_cols(const u32x4& d, const float (&m)[8],
+                                                  const uint32_t (&code)[8]) {
+  u32x2 c;
+  if constexpr (BF16) {
+    c = u32x2{encode4<FMT>(bf16_lo(d.x) * m[0], bf16_hi(d.x) * m[1], bf16_lo(d.y) * m[2],
+                           bf16_hi(d.y) * m[3]),
+              encode4<FMT>(bf16_lo(d.z) * m[4], bf16_hi(d.z) * m[5], bf16_lo(d.w) * m[6],
+                           bf16_hi(d.w) * m[7])};
+  } else {
+    c = u32x2{encode4<FMT>(__uint_as_float(d.x) * m[0], __uint_as_float(d.y) * m[1],
+                           __uint_as_float(d.z) * m[2], __uint_as_float(d.w) * m[3]), 0u};
+  }
+  constexpr int PER = BF16 ? 8 : 4;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (code[e] == 255u) {
+      const uint32_t sh = 8u * (e & 3);
+      c[e >> 2] = (c[e >> 2] & ~(0xFFu << sh)) | (0x7Fu << sh);
+    }
+  }
+  return c;
+}
+
+// |x| bit patterns of the elements of a piece, as fp32 bits (element e of 8 / 4).
+template <bool BF16>
+__device__ __forceinline__ void piece_abs(const u32x4& d, uint32_t (&a)[8]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[2 * k] = (d[k] & 0x7FFFu) << 16;
+      a[2 * k + 1] = d[k] & 0x7FFF0000u;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = d[k] & 0x7FFFFFFFu;
+  }
+}
+
+template <bool BF16, int FMT>
+__global__ __launch_bounds__(256) void mx_cast_transpose_kernel(
+    const void* __restrict__ xp, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ scales, uint8_t* __restrict__ qt, uint8_t* __restrict__ scales_t) {
+  constexpr int T = 128;
+  constexpr int PER = BF16 ? 8 : 4;   // elements per piece
+  constexpr int NP = 16 / PER;        // pieces per thread per pass
+  constexpr int PPR = T / PER;        // pieces per tile row
+  constexpr int PPB = 32 / PER;       // pieces per row block
+  __shared__ __attribute__((aligned(16))) uint8_t tile[T * T];
+  __shared__ uint32_t red[2][4][PPR][PER];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * T, r0 = (int64_t)blockIdx.y * T;
+  const int cc = (tid % PPR) * PER;  // this thread's columns in the tile
+  const int64_t nbr = cols / 32, nbc = rows / 32;  // blocks per row of q / of q_t
+#pragma unroll 1
+  for (int i = 0; i < 4; ++i) {
+    u32x4 v[NP];
+    int rr[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int u = 256 * (NP * i + k) + tid;
+      rr[k] = u / PPR;
+      v[k] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(xp) +
+                                             ((r0 + rr[k]) * cols + c0 + cc) * (BF16 ? 2 : 4));
+    }
+    // column amax of this pass (one column block), first over the thread's pieces
+    uint32_t ca[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      uint32_t a[8];
+      piece_abs<BF16>(v[k], a);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) ca[e] = max(ca[e], a[e]);
+    }
+    // ... then over the lanes holding the same columns (lane % PPR), then the waves
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      for (int o = PPR; o < 64; o <<= 1) ca[e] = max(ca[e], (uint32_t)__shfl_xor((int)ca[e], o));
+    }
+    if (lane < PPR) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) red[i & 1][wave][lane][e] = ca[e];
+    }
+    // rows: each piece is in one row block shared with PPB - 1 neighbouring lanes
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      uint32_t a = piece_amax<BF16>(v[k]);
+      a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+      a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+      if constexpr (PPB == 8) a = max(a, (uint32_t)__shfl_xor((int)a, 4));
+      const uint32_t code = mx_scale_code<FMT>(a);
+      u32x2 c;
+      if (code == 255u)
+        c = u32x2{0x7F7F7F7Fu, BF16 ? 0x7F7F7F7Fu : 0u};
+      else
+        c = piece_codes<BF16, FMT>(v[k], __uint_as_float((254u - code) << 23));
+      const int64_t off = (r0 + rr[k]) * cols + c0 + cc;
+      if constexpr (BF16)
+        *reinterpret_cast<u32x2*>(q + off) = c;
+      else
+        *reinterpret_cast<uint32_t*>(q + off) = c.x;
+      if ((tid & (PPB - 1)) == 0) scales[(r0 + rr[k]) * nbr + (c0 + cc) / 32] = (uint8_t)code;
+    }
+    __syncthreads();
+    uint32_t ccode[8];
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int l = tid % PPR;
+      const uint32_t a = max(max(red[i & 1][0][l][e], red[i & 1][1][l][e]),
+                             max(red[i & 1][2][l][e], red[i & 1][3][l][e]));
+      ccode[e] = mx_scale_code<FMT>(a);
+      m[e] = __uint_as_float(ccode[e] == 255u ? 0x3F800000u : (254u - ccode[e]) << 23);
+    }
+    if constexpr (!BF16) {
+#pragma unroll
+      for (int e = 4; e < 8; ++e) { ccode[e] = 0u; m[e] = 1.0f; }
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const u32x2 c = piece_codes_cols<BF16, FMT>(v[k], m, ccode);
+      if constexpr (BF16)
+        tile_park8(tile, rr[k], cc, c);
+      else
+        tile_park4(tile, rr[k], cc, c.x);
+    }
+    if (tid < PPR) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        scales_t[(c0 + cc + e) * nbc + r0 / 32 + i] = (uint8_t)ccode[e];
+    }
+  }
+  __syncthreads();
+  tile_store_qt<4>(tile, qt, rows, r0, c0, tid);
+}
+
+template <bool BF16, int FMT>
+static hipError_t launch_mx_t(const void* x, int64_t rows, int64_t cols, uint8_t* q,
+                              uint8_t* scales, uint8_t* qt, uint8_t* scales_t,
+                              hipStream_t stream) {
+  dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
+  hipLaunchKernelGGL((mx_cast_transpose_kernel<BF16, FMT>), grid, dim3(256), 0, stream, x, rows,
+                     cols, q, scales, qt, scales_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
+                                    uint8_t* q, uint8_t* scales, uint8_t* qt, uint8_t* scales_t,
+                                    hipStream_t stream) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (bf16)
+    return fmt == kE4M3 ? launch_mx_t<true, kE4M3>(x, rows, cols, q, scales, qt, scales_t, stream)
+                        : launch_mx_t<true, kE5M2>(x, rows, cols, q, scales, qt, scales_t, stream);
+  return fmt == kE4M3 ? launch_mx_t<false, kE4M3>(x, rows, cols, q, scales, qt, scales_t, stream)
+                      : launch_mx_t<false, kE5M2>(x, rows, cols, q, scales, qt, scales_t, stream);
+}
+
 template <bool BF16>
 static hipError_t launch_mx_b(const void* x, int64_t n, int fmt, uint8_t* q, uint8_t* scales,
                               hipStream_t stream) {

@@ -387,18 +387,26 @@ int fp8ds_gemm_rowcol(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t 
  */
 
 /*
- * fp8ds_cast_mx -- MXFP8 quantization of a [rows x cols] matrix along its rows.
+ * fp8ds_cast_mx -- MXFP8 quantization of a [rows x cols] matrix along its rows,
+ * optionally also of its transpose, from one read of x.
  *
- *   x        device, rows*cols elements of `xt`, row-major, 16-byte aligned.
- *   cols     a multiple of 32 (else FP8DS_ERR_SHAPE).
- *   q        device, rows*cols bytes, 16-byte aligned: the element codes.
- *   scales   device, rows*cols/32 bytes: the E8M0 code of block b of row r at
- *            [r * cols/32 + b].
- * A column-blocked copy (blocks along the other dimension) is this call on the
- * transposed matrix.  No amax, scale state or history is involved.
+ *   x          device, rows*cols elements of `xt`, row-major, 16-byte aligned.
+ *   cols       a multiple of 32 (else FP8DS_ERR_SHAPE).
+ *   q          device, rows*cols bytes, 16-byte aligned: the element codes.
+ *   scales     device, rows*cols/32 bytes: the E8M0 code of block b of row r at
+ *              [r * cols/32 + b].
+ *   q_t        device or NULL: [cols x rows] codes of x^T quantized along its rows
+ *              (blocks of 32 consecutive rows of a column of x), 16-byte aligned;
+ *              requires rows and cols to be multiples of 128 (else FP8DS_ERR_SHAPE).
+ *   scales_t   device [cols x rows/32] E8M0 codes of q_t; NULL exactly when q_t is.
+ * The GEMMs of a training step all run as fp8ds_gemm_mx (A B^T, both blocked
+ * along K): Y = X W takes (q of X, q_t of W); dX = dY W^T takes (q of dY, q of W);
+ * dW = X^T dY takes (q_t of X, q_t of dY).  No amax, scale state or history is
+ * involved.
  */
 int fp8ds_cast_mx(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
-                  uint8_t* q, uint8_t* scales, hipStream_t stream);
+                  uint8_t* q, uint8_t* scales, uint8_t* q_t, uint8_t* scales_t,
+                  hipStream_t stream);
 
 /*
  * fp8ds_gemm_mx -- MXFP8 GEMM  C = A B^T  with FP32 accumulation:

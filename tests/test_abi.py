@@ -151,13 +151,17 @@ def test_finer_scaling_validation_errors_without_gpu():
 def test_mx_validation_errors_without_gpu():
     L = dsg.lib()
     p = 0x1000
-    # fp8ds_cast_mx(x, xt, rows, cols, fmt, q, scales, stream)
-    assert L.fp8ds_cast_mx(p, 1, 4, 48, 0, p, p, None) == -2     # cols not a multiple of 32
-    assert L.fp8ds_cast_mx(p, 1, 4, 64, 5, p, p, None) == -3     # bad format
-    assert L.fp8ds_cast_mx(p, 9, 4, 64, 0, p, p, None) == -3     # bad dtype
-    assert L.fp8ds_cast_mx(p, 1, 4, 64, 0, p, None, None) == -1  # scales missing
-    assert L.fp8ds_cast_mx(p + 8, 1, 4, 64, 0, p, p, None) == -4
-    assert L.fp8ds_cast_mx(p, 1, 0, 64, 0, None, None, None) == 0  # empty: no-op
+    # fp8ds_cast_mx(x, xt, rows, cols, fmt, q, scales, q_t, scales_t, stream)
+    c = lambda *a: L.fp8ds_cast_mx(*a)
+    assert c(p, 1, 4, 48, 0, p, p, None, None, None) == -2     # cols not a multiple of 32
+    assert c(p, 1, 4, 64, 5, p, p, None, None, None) == -3     # bad format
+    assert c(p, 9, 4, 64, 0, p, p, None, None, None) == -3     # bad dtype
+    assert c(p, 1, 4, 64, 0, p, None, None, None, None) == -1  # scales missing
+    assert c(p + 8, 1, 4, 64, 0, p, p, None, None, None) == -4
+    assert c(p, 1, 0, 64, 0, None, None, None, None, None) == 0  # empty: no-op
+    assert c(p, 1, 128, 128, 0, p, p, p, None, None) == -1       # q_t without scales_t
+    assert c(p, 1, 96, 128, 0, p, p, p, p, None) == -2           # transposed copy: rows % 128
+    assert c(p, 1, 128, 128, 0, p, p, p + 4, p, None) == -4      # q_t misaligned
     # fp8ds_gemm_mx(M, N, K, A, fa, lda, sa, ldsa, B, fb, ldb, sb, ldsb, C, ct, ldc, amax, s)
     g = lambda K=256, lda=256, sa=p, ldsa=8, sb=p, C=p: L.fp8ds_gemm_mx(
         64, 64, K, p, 0, lda, sa, ldsa, p, 1, 256, sb, 8, C, 1, 64, None, None)

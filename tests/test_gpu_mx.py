@@ -1,7 +1,8 @@
-"""GPU parity of MXFP8 against the oracle (oracle/mx.py): the block cast (element
-codes and E8M0 scale codes bit-exact, zero / NaN / Inf / tiny blocks included)
-and the MX GEMM (accumulator bound on FP32 output, plus one BF16 ulp on BF16
-output; a NaN block poisons exactly its row)."""
+"""GPU parity of MXFP8 against the oracle (oracle/mx.py): the block cast and its
+transposed copy (element codes and E8M0 scale codes bit-exact, zero / NaN / Inf /
+tiny blocks included), the MX GEMM (accumulator bound on FP32 output, plus one
+BF16 ulp on BF16 output; a NaN block poisons exactly its row), and a whole MX
+training step (three casts with transposed copies, three NT GEMMs)."""
 
 import numpy as np
 import pytest
@@ -158,3 +159,81 @@ def test_mx_forward_full_size_sampled():
     np.testing.assert_array_equal(ws.cpu().numpy(), sw)
     acc, sum_abs = omx.mx_gemm_nt(cx, sx, dsg.E4M3, cw, sw, dsg.E4M3)
     check_bf16_out(bf16_bits(y)[rows], acc, sum_abs, omx.to_bf16(acc), 1.0, "mx forward")
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("fmt", [dsg.E4M3, dsg.E5M2])
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 128)])
+def test_mx_cast_transpose_matches_oracle(bf16, fmt, shape):
+    rows, cols = shape
+    x, xw = _input(rows, cols, 7 * rows + cols + fmt, bf16, specials=True)
+    xw = np.array(xw)  # add column specials: a zero, an Inf, a NaN and a tiny column block
+    xw[40:72, 9] = 0.0
+    xw[70, 17] = np.inf
+    xw[100, 30] = np.nan
+    xw[0:32, 50] *= np.float32(2.0**-100)
+    if bf16:
+        bits = workloads.to_bf16_bits(xw)
+        x = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+        xw = obf16.widen(bits).reshape(rows, cols)
+    else:
+        x = torch.from_numpy(np.ascontiguousarray(xw)).to(DEV)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=DEV)
+    qt = torch.empty((cols, rows), dtype=torch.uint8, device=DEV)
+    st = torch.empty((cols, rows // 32), dtype=torch.uint8, device=DEV)
+    dsg.fp8ds_cast_mx(x, fmt, q, s, qt, st)
+    torch.cuda.synchronize()
+    codes, scales = omx.mx_cast(xw, fmt)
+    codes_t, scales_t = omx.mx_cast(np.ascontiguousarray(xw.T), fmt)
+    np.testing.assert_array_equal(s.cpu().numpy(), scales)
+    np.testing.assert_array_equal(q.cpu().numpy(), codes)
+    np.testing.assert_array_equal(st.cpu().numpy(), scales_t)
+    np.testing.assert_array_equal(qt.cpu().numpy(), codes_t)
+
+
+def test_mx_training_step():
+    """Y = X W, dX = dY W^T, dW = X^T dY in MXFP8 (E4M3 forward, E5M2 gradient):
+    one transposing cast per tensor, three NT GEMMs, every output element against
+    the oracle's exact sums."""
+    M, K, N = 1024, 512, 256
+    x = workloads.normal(M * K, 301, 1.0).reshape(M, K)
+    w = workloads.normal(K * N, 302, 0.02).reshape(K, N)
+    dy = workloads.heavy_tail_grad(M * N, 303).reshape(M, N)
+    dev = {}
+    ref = {}
+    for name, a, fmt in (("x", x, dsg.E4M3), ("w", w, dsg.E4M3), ("dy", dy, dsg.E5M2)):
+        bits = workloads.to_bf16_bits(a)
+        t = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+        r, c = a.shape
+        q = torch.empty((r, c), dtype=torch.uint8, device=DEV)
+        s = torch.empty((r, c // 32), dtype=torch.uint8, device=DEV)
+        qt = torch.empty((c, r), dtype=torch.uint8, device=DEV)
+        st = torch.empty((c, r // 32), dtype=torch.uint8, device=DEV)
+        dsg.fp8ds_cast_mx(t, fmt, q, s, qt, st)
+        dev[name] = (q, s, qt, st, fmt)
+        aw = obf16.widen(bits).reshape(r, c)
+        ref[name] = omx.mx_cast(aw, fmt) + omx.mx_cast(np.ascontiguousarray(aw.T), fmt) + (fmt,)
+
+    def run(m, n, k, a, sa, fa, b, sb, fb):
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+        dsg.fp8ds_gemm_mx(m, n, k, a, fa, k, sa, k // 32, b, fb, k, sb, k // 32, c, n)
+        return c
+
+    X, W, D = dev["x"], dev["w"], dev["dy"]
+    y = run(M, N, K, X[0], X[1], X[4], W[2], W[3], W[4])      # X . (W^T blocked along K)
+    dx = run(M, K, N, D[0], D[1], D[4], W[0], W[1], W[4])     # dY . W  (blocked along N)
+    dw = run(K, N, M, X[2], X[3], X[4], D[2], D[3], D[4])     # X^T . dY^T (blocked along M)
+    torch.cuda.synchronize()
+    for name in ("x", "w", "dy"):
+        q, s, qt, st, _ = dev[name]
+        rc, rs, rct, rst, _ = ref[name]
+        for g, r in ((q, rc), (s, rs), (qt, rct), (st, rst)):
+            np.testing.assert_array_equal(g.cpu().numpy(), r)
+    X, W, D = ref["x"], ref["w"], ref["dy"]
+    for out, (a, sa, fa), (b, sb, fb), what in (
+            (y, (X[0], X[1], X[4]), (W[2], W[3], W[4]), "y"),
+            (dx, (D[0], D[1], D[4]), (W[0], W[1], W[4]), "dx"),
+            (dw, (X[2], X[3], X[4]), (D[2], D[3], D[4]), "dw")):
+        acc, sum_abs = omx.mx_gemm_nt(a, sa, fa, b, sb, fb)
+        check_bf16_out(bf16_bits(out), acc, sum_abs, omx.to_bf16(acc), 1.0, what)
