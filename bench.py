@@ -314,6 +314,16 @@ def finer_report(torch, dsg, x, w, dy=None, iters=10):
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     out["mx_gemm_fwd_nt"] = {"ms": round(ms, 4), "TFLOP/s": round(tflops, 1),
                              "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4)}
+
+    def mx_gemm_fp8():  # context: gfx950's block-scaled FP8 MFMA (not the exact datapath)
+        dsg.fp8ds_gemm_mx(M, N, K, xq, dsg.E4M3, K, xs, K // 32, wq, dsg.E4M3, K, ws, K // 32, y, N,
+                          amax_y, mma=dsg.MMA_FP8)
+
+    mx_gemm_fp8()
+    ms = time_launches(torch, stream, mx_gemm_fp8, iters)
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    out["mx_gemm_fwd_nt_fp8_mma"] = {"ms": round(ms, 4), "TFLOP/s": round(tflops, 1),
+                                     "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4)}
     del wt, xq, wq, y, xs, ws
     if dy is not None:
         out["mx_training_step"] = mx_step_report(torch, dsg, x, w, dy, iters)

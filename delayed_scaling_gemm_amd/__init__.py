@@ -77,7 +77,7 @@ def _declare(lib):
     lib.fp8ds_cast_mx.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.fp8ds_gemm_mx.restype = i32
     lib.fp8ds_gemm_mx.argtypes = [i64, i64, i64, vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, vp,
-                                  i32, i64, vp, vp]
+                                  i32, i64, vp, i32, vp]
     lib.fp8ds_gemm_batched.restype = i32
     lib.fp8ds_gemm_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i32, i64, i64, vp, vp, i32,
                                        i64, i64, vp, vp, i32, i64, i64, vp, i32, vp]
@@ -421,7 +421,7 @@ def fp8ds_cast_mx(x, fmt, q, scales, q_t=None, scales_t=None, stream=None):
 
 
 def fp8ds_gemm_mx(M, N, K, a, fa, lda, scales_a, ld_scales_a, b, fb, ldb, scales_b, ld_scales_b,
-                  c, ldc, amax_c=None, stream=None):
+                  c, ldc, amax_c=None, stream=None, mma=MMA_EXACT):
     """MXFP8 GEMM ``C = A B^T``: A [M, K] and B [N, K] element codes with E8M0
     block scales [M, ld_scales_a] / [N, ld_scales_b] along K; K a multiple of 128."""
     import torch
@@ -434,7 +434,7 @@ def fp8ds_gemm_mx(M, N, K, a, fa, lda, scales_a, ld_scales_a, b, fb, ldb, scales
     _need(amax_c, "amax_c", (torch.float32,), 1)
     _check(lib().fp8ds_gemm_mx(M, N, K, _ptr(a), fa, lda, _ptr(scales_a), ld_scales_a, _ptr(b), fb,
                                ldb, _ptr(scales_b), ld_scales_b, _ptr(c), _dtype_code(c), ldc,
-                               _ptr(amax_c), _stream(stream)))
+                               _ptr(amax_c), mma, _stream(stream)))
 
 
 def abi_version() -> int:

@@ -447,8 +447,10 @@ int fp8ds_cast_mx(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8
 int fp8ds_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* A, fp8ds_format fa, int64_t lda,
                   const uint8_t* scales_a, int64_t ld_scales_a, const uint8_t* B, fp8ds_format fb,
                   int64_t ldb, const uint8_t* scales_b, int64_t ld_scales_b, void* C,
-                  fp8ds_dtype ct, int64_t ldc, float* amax_c, hipStream_t stream) {
+                  fp8ds_dtype ct, int64_t ldc, float* amax_c, fp8ds_mma mma, hipStream_t stream) {
   const char* who = "fp8ds_gemm_mx";
+  if (mma != FP8DS_MMA_EXACT && mma != FP8DS_MMA_FP8)
+    return fail(FP8DS_ERR_ENUM, "%s: bad mma %d", who, (int)mma);
   if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8DS_ERR_ENUM, "%s: bad format", who);
   if (!valid_dtype(ct)) return fail(FP8DS_ERR_ENUM, "%s: bad output dtype", who);
   const int64_t lim = int64_t(1) << 31;
@@ -489,7 +491,7 @@ int fp8ds_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* A, fp8ds_forma
     p.C = C; p.out_bf16 = ct == FP8DS_BF16; p.ldc = ldc; p.amax_c = amax_c;
     p.batch = 1; p.stride_a = 0; p.stride_b = 0; p.stride_c = 0;
     p.sc_a = scales_a; p.sc_b = scales_b; p.ldsa = ld_scales_a; p.ldsb = ld_scales_b;
-    e = fp8ds::launch_gemm_mx(p, num_cus(), stream);
+    e = fp8ds::launch_gemm_mx(p, mma == FP8DS_MMA_EXACT, num_cus(), stream);
   }
   return hip_status(e, who);
 }

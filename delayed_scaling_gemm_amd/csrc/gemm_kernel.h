@@ -592,8 +592,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT,
           bool VS = false, bool MX = false>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
-  static_assert(!MX || (EXACT && DIRECT && A_KC && B_KC && !VS),
-                "MX blocks run along K: both operands K-contiguous, direct loads, exact path");
+  static_assert(!MX || (DIRECT && A_KC && B_KC && !VS),
+                "MX blocks run along K: both operands K-contiguous, direct loads");
   constexpr int NT = 256;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -837,9 +837,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   } else {
     u32x4 ra[2][FM][2], rb[2][FN][2];  // two chunks per step, by step parity
     // Step s of a stage takes, per lane, 32 consecutive K values of its row:
-    // k = 64 (l / 32) + 32 s + [0, 32).  K-major tiles give them as two 16-byte
-    // chunks; MN-major tiles (direct loads of MN-contiguous operands) as four
-    // transposing 8-byte reads.
+    // k = 64 (l / 32) + 32 s + [0, 32) (MX: the chunks described at `mma`).
+    // K-major tiles give them as two 16-byte chunks; MN-major tiles (direct loads
+    // of MN-contiguous operands) as four transposing 8-byte reads.
     auto read_mn32 = [&](const uint8_t* tile, auto rows_tag, int r0, int s, u32x4 (&x)[2]) {
       constexpr int R = decltype(rows_tag)::value;
 #pragma unroll
@@ -858,7 +858,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
             xb[j][t] = *reinterpret_cast<const u32x4*>(
-                lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, fc + 2 * s + t));
+                lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, MX ? 4 * s + 2 * t + (lane >> 5)
+                                                                : fc + 2 * s + t));
         }
       }
 #pragma unroll
@@ -869,11 +870,35 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
             xa[i][t] = *reinterpret_cast<const u32x4*>(
-                lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, fc + 2 * s + t));
+                lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, MX ? 4 * s + 2 * t + (lane >> 5)
+                                                                : fc + 2 * s + t));
         }
       }
     };
-    auto mma = [&](const u32x4 (&xa)[FM][2], const u32x4 (&xb)[FN][2]) {
+    // MX: this lane's E8M0 scale dwords (the 4 blocks of a stage per row), loaded
+    // a stage ahead.  The block-scaled instruction (probed on gfx950) scales
+    // bytes 0..15 of lanes r and r + 32 by lane r's scale and bytes 16..31 of both
+    // by lane r + 32's: each of its two K blocks is the first or the second 16
+    // bytes of the two lanes of a row.  Step s therefore gives lane (r, h) the
+    // chunks 4 s + h (bytes 0..15) and 4 s + 2 + h (bytes 16..31): the halves of
+    // stage blocks 2 s and 2 s + 1, whose scales lanes h = 0 and h = 1 hand over.
+    uint32_t fsa_cur[FM], fsb_cur[FN], fsa_nxt[FM], fsb_nxt[FN];
+    auto load_scales8 = [&](int kt) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int64_t r = min(m0 + wm * WTM + i * 32 + fr, M - 1);
+          fsa_nxt[i] = *reinterpret_cast<const uint32_t*>(p.sc_a + r * p.ldsa + 4 * (int64_t)kt);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t r = min(n0 + wn * WTN + j * 32 + fr, N - 1);
+          fsb_nxt[j] = *reinterpret_cast<const uint32_t*>(p.sc_b + r * p.ldsb + 4 * (int64_t)kt);
+        }
+      }
+    };
+    auto mma = [&](const u32x4 (&xa)[FM][2], const u32x4 (&xb)[FN][2], int s) {
+      const int sh = 16 * s + 8 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const v8i af = v8i{(int)xa[i][0][0], (int)xa[i][0][1], (int)xa[i][0][2], (int)xa[i][0][3],
@@ -883,13 +908,21 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
           const v8i bf = v8i{(int)xb[j][0][0], (int)xb[j][0][1], (int)xb[j][0][2],
                              (int)xb[j][0][3], (int)xb[j][1][0], (int)xb[j][1][1],
                              (int)xb[j][1][2], (int)xb[j][1][3]};
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[i][j], FB, FA,
-                                                                       0, 0, 0, 0);
+          if constexpr (MX) {
+            const int scb = (int)__builtin_amdgcn_ubfe(fsb_cur[j], sh, 8);
+            const int sca = (int)__builtin_amdgcn_ubfe(fsa_cur[i], sh, 8);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[i][j], FB, FA,
+                                                                         0, scb, 0, sca);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[i][j], FB, FA,
+                                                                         0, 0, 0, 0);
+          }
         }
       }
     };
     if (nk > 0) {
       if constexpr (DIRECT) {
+        load_scales8(0);
         issue_direct(0, 0);
         if (nk > 1) issue_direct(1, 1);
         vmem_wait_all();
@@ -909,12 +942,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         la.load(A, p.lda, m0, M, (int64_t)(kt + 1) * KB, K, tid);
         lb.load(B, p.ldb, n0, N, (int64_t)(kt + 1) * KB, K, tid);
       }
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fsa_cur[i] = fsa_nxt[i];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fsb_cur[j] = fsb_nxt[j];
+        if constexpr (MORE) load_scales8(kt + 1);
+      }
       read_step(cur, 1, ra[1], rb[1]);
       if constexpr (MORE && !DIRECT) {
         la.store(lds_a[cur ^ 1], tid);
         lb.store(lds_b[cur ^ 1], tid);
       }
-      mma(ra[0], rb[0]);
+      mma(ra[0], rb[0], 0);
       if constexpr (MORE) {
         if constexpr (DIRECT) vmem_wait_all();
         __syncthreads();
@@ -923,7 +963,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
           if (kt + 2 < nk) issue_direct(kt + 2, cur);
         }
       }
-      mma(ra[1], rb[1]);
+      mma(ra[1], rb[1], 1);
     };
     for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
     if (nk > 0) stage(nk - 1, std::false_type{});

@@ -104,8 +104,8 @@ hipError_t launch_gemm_fp8(const GemmProblem& p, int num_cus, hipStream_t stream
 hipError_t launch_gemm_rowcol(const GemmProblem& p, int num_cus, hipStream_t stream);
 // MXFP8 GEMM C = A B^T (opa N, opb T), A and B blocked along K with E8M0 scales
 // p.sc_a / p.sc_b; K a multiple of 128, operands 16-byte aligned, batch 1.
-// EXACT datapath with the scales folded into the BF16 widening.
-hipError_t launch_gemm_mx(const GemmProblem& p, int num_cus, hipStream_t stream);
+// exact: scales folded into the BF16 widening; else the block-scaled FP8 MFMA.
+hipError_t launch_gemm_mx(const GemmProblem& p, bool exact, int num_cus, hipStream_t stream);
 
 // MXFP8 cast of n elements (blocks of 32 consecutive elements): q [n], scales [n / 32].
 hipError_t launch_mx_cast(const void* x, bool bf16, int64_t n, int fmt, uint8_t* q,

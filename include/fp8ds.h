@@ -427,11 +427,15 @@ int fp8ds_cast_mx(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8
  *   K          a multiple of 128 (four blocks per pipeline stage), else FP8DS_ERR_SHAPE.
  *   A, B, C, lda, ldb, ldc * element size: 16-byte aligned; the scale arrays and
  *   ld_scales_a / ld_scales_b: 4-byte aligned (FP8DS_ERR_ALIGN otherwise).
+ *   mma        FP8DS_MMA_EXACT (the BF16 widening above, default) or FP8DS_MMA_FP8:
+ *              gfx950's block-scaled FP8 matrix instruction, each lane passing the
+ *              E8M0 scale of its 32 K values, at twice the rate and with the FP8
+ *              instructions' summation precision (see fp8ds_mma).
  */
 int fp8ds_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* A, fp8ds_format fa, int64_t lda,
                   const uint8_t* scales_a, int64_t ld_scales_a, const uint8_t* B, fp8ds_format fb,
                   int64_t ldb, const uint8_t* scales_b, int64_t ld_scales_b, void* C,
-                  fp8ds_dtype ct, int64_t ldc, float* amax_c, hipStream_t stream);
+                  fp8ds_dtype ct, int64_t ldc, float* amax_c, fp8ds_mma mma, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -162,9 +162,9 @@ def test_mx_validation_errors_without_gpu():
     assert c(p, 1, 128, 128, 0, p, p, p, None, None) == -1       # q_t without scales_t
     assert c(p, 1, 96, 128, 0, p, p, p, p, None) == -2           # transposed copy: rows % 128
     assert c(p, 1, 128, 128, 0, p, p, p + 4, p, None) == -4      # q_t misaligned
-    # fp8ds_gemm_mx(M, N, K, A, fa, lda, sa, ldsa, B, fb, ldb, sb, ldsb, C, ct, ldc, amax, s)
-    g = lambda K=256, lda=256, sa=p, ldsa=8, sb=p, C=p: L.fp8ds_gemm_mx(
-        64, 64, K, p, 0, lda, sa, ldsa, p, 1, 256, sb, 8, C, 1, 64, None, None)
+    # fp8ds_gemm_mx(M, N, K, A, fa, lda, sa, ldsa, B, fb, ldb, sb, ldsb, C, ct, ldc, amax, mma, s)
+    g = lambda K=256, lda=256, sa=p, ldsa=8, sb=p, C=p, mma=0: L.fp8ds_gemm_mx(
+        64, 64, K, p, 0, lda, sa, ldsa, p, 1, 256, sb, 8, C, 1, 64, None, mma, None)
     assert g(K=192, lda=192) == -2   # K not a multiple of 128
     assert g(lda=128) == -2          # lda < K
     assert g(ldsa=4) == -2           # scale leading dimension < K / 32
@@ -172,5 +172,6 @@ def test_mx_validation_errors_without_gpu():
     assert g(C=None) == -1
     assert g(sb=p + 2) == -4         # scale array not 4-byte aligned
     assert g(ldsa=10) == -4          # scale leading dimension not a multiple of 4
-    assert L.fp8ds_gemm_mx(64, 64, 256, p, 7, 256, p, 8, p, 0, 256, p, 8, p, 1, 64, None,
+    assert L.fp8ds_gemm_mx(64, 64, 256, p, 7, 256, p, 8, p, 0, 256, p, 8, p, 1, 64, None, 0,
                            None) == -3
+    assert g(mma=5) == -3

@@ -14,7 +14,7 @@ import workloads  # noqa: E402
 from oracle import bf16 as obf16  # noqa: E402
 from oracle import mx as omx  # noqa: E402
 from tests.parity import bf16_bits, check_acc, check_bf16_out  # noqa: E402
-from tests.test_gpu_gemm import finite_codes  # noqa: E402
+from tests.test_gpu_gemm import FP8_PATH_REL, finite_codes, int_codes  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -72,7 +72,7 @@ def test_mx_cast_full_size_sampled():
     np.testing.assert_array_equal(q.cpu().numpy()[rows], codes)
 
 
-def _gemm(a, sa, fa, b, sb, fb, out=torch.bfloat16):
+def _gemm(a, sa, fa, b, sb, fb, out=torch.bfloat16, mma=dsg.MMA_EXACT):
     M, K = a.shape
     N = b.shape[0]
     A, B = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
@@ -80,7 +80,7 @@ def _gemm(a, sa, fa, b, sb, fb, out=torch.bfloat16):
     ldc = (N + 7) // 8 * 8  # 16-byte rows for BF16 and FP32 outputs
     C = torch.empty((M, ldc), dtype=out, device=DEV)
     am = torch.zeros(1, device=DEV)
-    dsg.fp8ds_gemm_mx(M, N, K, A, fa, K, SA, K // 32, B, fb, K, SB, K // 32, C, ldc, am)
+    dsg.fp8ds_gemm_mx(M, N, K, A, fa, K, SA, K // 32, B, fb, K, SB, K // 32, C, ldc, am, mma=mma)
     torch.cuda.synchronize()
     return C[:, :N], float(am.item())
 
@@ -237,3 +237,36 @@ def test_mx_training_step():
             (dw, (X[2], X[3], X[4]), (D[2], D[3], D[4]), "dw")):
         acc, sum_abs = omx.mx_gemm_nt(a, sa, fa, b, sb, fb)
         check_bf16_out(bf16_bits(out), acc, sum_abs, omx.to_bf16(acc), 1.0, what)
+
+
+# ---------------------------------------------------------------- FP8 datapath (opt-in)
+# gfx950's block-scaled FP8 MFMA: exact where no product falls out of its
+# summation window, otherwise within the FP8 datapath's measured bound.
+
+@pytest.mark.parametrize("fa,fb", FMT_PAIRS)
+@pytest.mark.parametrize("M,N", [(256, 256), (100, 200)])
+def test_mx_fp8_path_small_integers_exact(fa, fb, M, N):
+    """Small integers with block scales 2^-2 .. 2^2: every product, group sum and
+    FP32 total is exact, so the result equals the oracle bit for bit (this also
+    pins which byte of the scale register belongs to which block)."""
+    K = 128
+    rng = np.random.default_rng(M + N + fa + 2 * fb)
+    a, _ = int_codes(rng, (M, K), fa)
+    b, _ = int_codes(rng, (N, K), fb)
+    sa = rng.integers(125, 130, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(125, 130, (N, K // 32)).astype(np.uint8)
+    acc, _ = omx.mx_gemm_nt(a, sa, fa, b, sb, fb)
+    c, _ = _gemm(a, sa, fa, b, sb, fb, out=torch.float32, mma=dsg.MMA_FP8)
+    np.testing.assert_array_equal(c.cpu().numpy().astype(np.float64), acc)
+
+
+@pytest.mark.parametrize("fa,fb", FMT_PAIRS)
+@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (300, 600, 1024)])
+def test_mx_fp8_path_within_bound(fa, fb, M, N, K):
+    rng = np.random.default_rng(3 * M + N + K + fa)
+    a, b = finite_codes(rng, (M, K), fa), finite_codes(rng, (N, K), fb)
+    sa = rng.integers(112, 143, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(112, 143, (N, K // 32)).astype(np.uint8)
+    acc, sum_abs = omx.mx_gemm_nt(a, sa, fa, b, sb, fb)
+    c32, _ = _gemm(a, sa, fa, b, sb, fb, out=torch.float32, mma=dsg.MMA_FP8)
+    check_acc(c32.cpu().numpy(), acc, sum_abs, "mx fp8 path", FP8_PATH_REL)
