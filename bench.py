@@ -331,43 +331,23 @@ def finer_report(torch, dsg, x, w, dy=None, iters=10):
 
 
 def mx_step_report(torch, dsg, x, w, dy, iters):
-    """A whole MXFP8 training step of the Linear: one cast per tensor with its
-    transposed copy (X, W E4M3; dY E5M2), then Y = X W, dX = dY W^T, dW = X^T dY,
-    all as NT MX GEMMs (blocks along K)."""
-    dev = x.device
+    """A whole MXFP8 training step of the Linear (MXLinear): one cast per tensor
+    with its transposed copy (X, W E4M3; dY E5M2), then Y = X W, dX = dY W^T and
+    dW = X^T dY, all as NT MX GEMMs (blocks along K)."""
+    from delayed_scaling_gemm_amd.linear import MXLinear
+
     M, K = x.shape
-    N = w.shape[1]
-    bufs = {}
-    for name, t, fmt in (("x", x, dsg.E4M3), ("w", w, dsg.E4M3), ("dy", dy, dsg.E5M2)):
-        r, c = t.shape
-        bufs[name] = (t, fmt, torch.empty(r, c, dtype=torch.uint8, device=dev),
-                      torch.empty(r, c // 32, dtype=torch.uint8, device=dev),
-                      torch.empty(c, r, dtype=torch.uint8, device=dev),
-                      torch.empty(c, r // 32, dtype=torch.uint8, device=dev))
-    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
-    dw = torch.empty(K, N, dtype=torch.bfloat16, device=dev)
-    X, W, D = bufs["x"], bufs["w"], bufs["dy"]
-
-    def step():
-        for t, fmt, q, s, qt, st in bufs.values():
-            dsg.fp8ds_cast_mx(t, fmt, q, s, qt, st)
-        dsg.fp8ds_gemm_mx(M, N, K, X[2], X[1], K, X[3], K // 32, W[4], W[1], K, W[5], K // 32, y, N)
-        dsg.fp8ds_gemm_mx(M, K, N, D[2], D[1], N, D[3], N // 32, W[2], W[1], N, W[3], N // 32, dx, K)
-        dsg.fp8ds_gemm_mx(K, N, M, X[4], X[1], M, X[5], M // 32, D[4], D[1], M, D[5], M // 32, dw, N)
-
-    step()
-    ms = time_launches(torch, stream=torch.cuda.current_stream(), fn=step, iters=iters)
-    cast_ms = time_launches(torch, torch.cuda.current_stream(),
-                            lambda: dsg.fp8ds_cast_mx(*X), iters)
-    res = {"ms": round(ms, 4), "TFLOP/s": round(6.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
+    lin = MXLinear(device=x.device)
+    stream = torch.cuda.current_stream()
+    lin.step(x, w, dy)
+    ms = time_launches(torch, stream, lambda: lin.step(x, w, dy), iters)
+    cast_ms = time_launches(torch, stream, lambda: lin._cast(0, "x", x, None), iters)
+    res = {"ms": round(ms, 4), "TFLOP/s": round(6.0 * M * w.shape[1] * K / (ms * 1e-3) / 1e12, 1),
            "cast_x_with_transpose_ms": round(cast_ms, 4),
            "cast_x_with_transpose_GB/s": round(4.0625 * M * K / (cast_ms * 1e-3) / 1e9, 1)}
-    del bufs, y, dx, dw
+    del lin
     torch.cuda.empty_cache()
     return res
-    torch.cuda.empty_cache()
-    return out
 
 
 def configs_report(torch, dsg, workloads, dev, iters=5):

@@ -29,8 +29,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (ALGO_MAX, E4M3, E5M2, HEALTH_COUNTS, HEALTH_NAMES, OP_N, OP_T, fp8ds_adamw,
-               fp8ds_cast, fp8ds_cast_health, fp8ds_gemm, fp8ds_scale_update)
+from . import (ALGO_MAX, E4M3, E5M2, HEALTH_COUNTS, HEALTH_NAMES, MMA_EXACT, OP_N, OP_T,
+               fp8ds_adamw, fp8ds_cast, fp8ds_cast_health, fp8ds_cast_mx, fp8ds_gemm,
+               fp8ds_gemm_mx, fp8ds_scale_update)
 
 X, W, DY = 0, 1, 2
 
@@ -262,3 +263,64 @@ class BatchedDelayedScalingLinear:
         fp8ds_scale_update(self.history, self.cursor, am, [self.fmt] * (2 * B), self.algo,
                            self.margin, s, None, stream)
         return {"xq": xq, "wq": wq, "y": y}
+
+
+class MXLinear:
+    """The same Linear step in MXFP8 ("FP8 混合精度训练工程实践" §九: blocks of 32
+    values along the contraction sharing an E8M0 scale).  There is no scaling
+    state: every block's scale comes from the block itself.  Each tensor is cast
+    once with its transposed copy (fp8ds_cast_mx), which gives every product
+    both operands blocked along its own K:
+
+      Y  = X W        fp8ds_gemm_mx(q of X,     q_t of W)    K = in
+      dX = dY W^T     fp8ds_gemm_mx(q of dY,    q of W)      K = out
+      dW = X^T dY     fp8ds_gemm_mx(q_t of X,   q_t of dY)   K = tokens
+
+    Shapes: tokens, in and out multiples of 128.  ``mma`` picks the GEMM
+    datapath (exact BF16 widening, or the block-scaled FP8 instruction)."""
+
+    def __init__(self, fmts=(E4M3, E4M3, E5M2), device="cuda", mma: int = MMA_EXACT):
+        self.fmts = tuple(fmts)
+        self.device = torch.device(device)
+        self.mma = mma
+        self._bufs = {}
+        self.amax_y = torch.zeros(1, dtype=torch.float32, device=self.device)
+
+    def _buf(self, name, shape, dtype):
+        b = self._bufs.get(name)
+        if b is None or tuple(b.shape) != tuple(shape) or b.dtype != dtype:
+            b = torch.empty(shape, dtype=dtype, device=self.device)
+            self._bufs[name] = b
+        return b
+
+    def _cast(self, t, name, x, stream):
+        r, c = x.shape
+        u8 = torch.uint8
+        q, s = self._buf(name + "q", (r, c), u8), self._buf(name + "s", (r, c // 32), u8)
+        qt, st = self._buf(name + "qt", (c, r), u8), self._buf(name + "st", (c, r // 32), u8)
+        fp8ds_cast_mx(x, self.fmts[t], q, s, qt, st, stream)
+        return q, s, qt, st
+
+    def _gemm(self, m, n, k, a, sa, fa, b, sb, fb, out, stream, amax=None):
+        fp8ds_gemm_mx(m, n, k, a, fa, k, sa, k // 32, b, fb, k, sb, k // 32, out, n, amax, stream,
+                      self.mma)
+
+    def step(self, x, w, dy=None, stream=None):
+        """x [M, K], w [K, N] (and dy [M, N]), BF16 or FP32 on the device.
+        Returns the BF16 outputs y (and dx, dw) and the MX copies of the inputs."""
+        M, K = x.shape
+        N = w.shape[1]
+        bf = torch.bfloat16
+        xq, xs, xqt, xst = self._cast(X, "x", x, stream)
+        wq, ws, wqt, wst = self._cast(W, "w", w, stream)
+        y = self._buf("y", (M, N), bf)
+        self._gemm(M, N, K, xq, xs, self.fmts[X], wqt, wst, self.fmts[W], y, stream, self.amax_y)
+        out = {"y": y, "xq": xq, "xs": xs, "xqt": xqt, "xst": xst, "wq": wq, "ws": ws,
+               "wqt": wqt, "wst": wst}
+        if dy is not None:
+            dyq, dys, dyqt, dyst = self._cast(DY, "dy", dy, stream)
+            dx, dw = self._buf("dx", (M, K), bf), self._buf("dw", (K, N), bf)
+            self._gemm(M, K, N, dyq, dys, self.fmts[DY], wq, ws, self.fmts[W], dx, stream)
+            self._gemm(K, N, M, xqt, xst, self.fmts[X], dyqt, dyst, self.fmts[DY], dw, stream)
+            out.update(dx=dx, dw=dw, dyq=dyq, dys=dys, dyqt=dyqt, dyst=dyst)
+        return out

@@ -270,3 +270,36 @@ def test_mx_fp8_path_within_bound(fa, fb, M, N, K):
     acc, sum_abs = omx.mx_gemm_nt(a, sa, fa, b, sb, fb)
     c32, _ = _gemm(a, sa, fa, b, sb, fb, out=torch.float32, mma=dsg.MMA_FP8)
     check_acc(c32.cpu().numpy(), acc, sum_abs, "mx fp8 path", FP8_PATH_REL)
+
+
+def test_mx_linear_matches_the_raw_calls():
+    """MXLinear.step issues exactly the casts and GEMMs of test_mx_training_step:
+    its outputs equal those of the C-ABI calls made one by one, bit for bit."""
+    from delayed_scaling_gemm_amd.linear import MXLinear
+
+    M, K, N = 512, 256, 384
+    x = torch.randn(M, K, device=DEV).to(torch.bfloat16)
+    w = (0.02 * torch.randn(K, N, device=DEV)).to(torch.bfloat16)
+    dy = (1e-3 * torch.randn(M, N, device=DEV)).to(torch.bfloat16)
+    out = MXLinear(device=DEV).step(x, w, dy)
+    torch.cuda.synchronize()
+    casts = {}
+    for name, t, fmt in (("x", x, dsg.E4M3), ("w", w, dsg.E4M3), ("dy", dy, dsg.E5M2)):
+        r, c = t.shape
+        q, s = _cast(t, fmt)
+        qt = torch.empty((c, r), dtype=torch.uint8, device=DEV)
+        st = torch.empty((c, r // 32), dtype=torch.uint8, device=DEV)
+        q2 = torch.empty_like(q)
+        s2 = torch.empty_like(s)
+        dsg.fp8ds_cast_mx(t, fmt, q2, s2, qt, st)
+        torch.cuda.synchronize()
+        assert torch.equal(q, q2) and torch.equal(s, s2)
+        casts[name] = (q, s, qt, st, fmt)
+    X, W, D = casts["x"], casts["w"], casts["dy"]
+    for key, (m, n, k, a, b) in {"y": (M, N, K, (X[0], X[1], X[4]), (W[2], W[3], W[4])),
+                                 "dx": (M, K, N, (D[0], D[1], D[4]), (W[0], W[1], W[4])),
+                                 "dw": (K, N, M, (X[2], X[3], X[4]), (D[2], D[3], D[4]))}.items():
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+        dsg.fp8ds_gemm_mx(m, n, k, a[0], a[2], k, a[1], k // 32, b[0], b[2], k, b[1], k // 32, c, n)
+        torch.cuda.synchronize()
+        assert torch.equal(out[key].view(torch.int16), c.view(torch.int16)), key
