@@ -7,11 +7,12 @@
 // "LLM FP8 微调上线生产实战" §核心原理), so the input is read once.
 //
 // Design for gfx950: the pass is HBM-bound (2 or 4 bytes read, 1 written per
-// element).  Each thread moves 16 elements per step with 16-byte vector loads and
-// one 16-byte store; a grid-stride loop over ~8 workgroups per CU keeps enough
-// bytes in flight.  amax is an integer max over |x| bit patterns (exact and order
-// independent), reduced by wave shuffles, then LDS, then one global atomic per
-// workgroup.  The saturation count is reduced the same way with integer adds.
+// element).  Threads move lane-contiguous 16-byte pieces of input, issuing all
+// their loads before converting, in a one-shot grid (each workgroup covers a
+// fixed contiguous range once).  amax is an integer max over |x| bit patterns
+// (exact and order independent), reduced by wave shuffles, then LDS, then at
+// most one global atomic per workgroup.  The saturation count is reduced the
+// same way with integer adds.
 
 #include "cast_common.h"
 #include "launch.h"
@@ -62,22 +63,26 @@ struct CastArgs {
 // it out of the caches measured faster).  A launch covers the whole tensor once
 // (no grid-stride loop), so workgroups retire in address order and new ones
 // start at once.  Atomics on one address serialise (about 11 ns each), so
-// workgroups are large (1024 threads: few resident workgroups all meeting the
-// freshly reset amax at once) and skip the amax atomic when the global value
-// already covers theirs (see block_commit).  Pieces whose group partners lie
-// past the end, and the last fewer-than-one-piece elements, go element by element.
-#ifndef FP8DS_CAST_GROUPS
-#define FP8DS_CAST_GROUPS 4
-#endif
-#ifndef FP8DS_CAST_THREADS
-#define FP8DS_CAST_THREADS 1024
-#endif
-template <bool BF16>
+// workgroups skip the amax atomic when the global value already covers theirs
+// (see block_commit).  Pieces whose group partners lie past the end, and the last
+// fewer-than-one-piece elements, go element by element.
+//
+// Workgroup shape (threads T, groups per thread G), measured on the box over
+// BF16 casts: 1024 x 4 (64 Ki elements per workgroup) is best on tensors of
+// tens of millions of elements, where it makes exactly two rounds of two
+// resident workgroups per CU on a 4096 x 16384 tensor; 256 x 8 (32 Ki) is 5-7%
+// faster on 2^30 elements, where the rounds are many and more, smaller
+// workgroups keep more loads in flight per CU (6.1-6.2 against 5.8-5.9 TB/s).
+// The counting cast (STATS) and the amax alone stay at 1024 x 4 at every size:
+// with their extra registers 256 x 8 measured 13% and 3% slower there.
+constexpr int64_t kCastLargeElems = int64_t(1) << 28;  // from here on: 256 x 8
+
+template <bool BF16, int T, int G>
 struct CastGroups {
-  static constexpr int kGroups = FP8DS_CAST_GROUPS;    // 16-element groups per thread
-  static constexpr int kThreads = FP8DS_CAST_THREADS;  // threads per workgroup
-  static constexpr int kPer = BF16 ? 8 : 4;            // elements per 16-byte piece
-  static constexpr int kPieces = 16 / kPer;            // pieces per group
+  static constexpr int kGroups = G;             // 16-element groups per thread
+  static constexpr int kThreads = T;            // threads per workgroup
+  static constexpr int kPer = BF16 ? 8 : 4;     // elements per 16-byte piece
+  static constexpr int kPieces = 16 / kPer;     // pieces per group
 };
 
 // One element of the cast (ragged pieces and tails): amax bits, saturation and
@@ -109,9 +114,9 @@ __device__ __forceinline__ void cast1(const void* x, uint8_t* q, int64_t i, floa
   }
 }
 
-template <bool BF16, int FMT, bool WRITE_Q, bool STATS>
-__global__ __launch_bounds__(CastGroups<BF16>::kThreads) void cast_kernel(CastArgs p) {
-  using CG = CastGroups<BF16>;
+template <bool BF16, int FMT, bool WRITE_Q, bool STATS, int TH, int GR>
+__global__ __launch_bounds__(TH) void cast_kernel(CastArgs p) {
+  using CG = CastGroups<BF16, TH, GR>;
   constexpr int G = CG::kGroups, T = CG::kThreads, PER = CG::kPer, NP = CG::kPieces;
   __shared__ uint32_t red[(STATS ? 6 : 2) * (T / 64)];
   Health h;
@@ -314,16 +319,26 @@ hipError_t launch_prologue(int64_t count, const float* scale, float* scale_used,
   return hipGetLastError();
 }
 
-template <bool BF16, int FMT, bool WRITE_Q, bool STATS>
-static hipError_t launch_cast_t(const CastArgs& a, int64_t batch, hipStream_t stream) {
-  using CG = CastGroups<BF16>;
+template <bool BF16, int FMT, bool WRITE_Q, bool STATS, int TH, int GR>
+static hipError_t launch_cast_shape(const CastArgs& a, int64_t batch, hipStream_t stream) {
+  using CG = CastGroups<BF16, TH, GR>;
   constexpr int64_t per_block = (int64_t)CG::kThreads * CG::kGroups * CG::kPieces;  // pieces
   const int64_t pieces = a.n / CG::kPer;
   int64_t gx = (pieces + per_block - 1) / per_block;
   if (gx < 1) gx = 1;  // block 0 also takes the ragged tail (fewer than one piece)
-  hipLaunchKernelGGL((cast_kernel<BF16, FMT, WRITE_Q, STATS>), dim3((unsigned)gx, (unsigned)batch),
-                     dim3((unsigned)CG::kThreads), 0, stream, a);
+  hipLaunchKernelGGL((cast_kernel<BF16, FMT, WRITE_Q, STATS, TH, GR>),
+                     dim3((unsigned)gx, (unsigned)batch), dim3((unsigned)CG::kThreads), 0, stream,
+                     a);
   return hipGetLastError();
+}
+
+template <bool BF16, int FMT, bool WRITE_Q, bool STATS>
+static hipError_t launch_cast_t(const CastArgs& a, int64_t batch, hipStream_t stream) {
+  if constexpr (WRITE_Q && !STATS) {
+    if (a.n >= kCastLargeElems)
+      return launch_cast_shape<BF16, FMT, WRITE_Q, STATS, 256, 8>(a, batch, stream);
+  }
+  return launch_cast_shape<BF16, FMT, WRITE_Q, STATS, 1024, 4>(a, batch, stream);
 }
 
 template <bool BF16, bool STATS>

@@ -221,3 +221,34 @@ def test_stress_tensor_full_size(fmt):
     pos = np.unique(np.concatenate([pos, big, np.arange(64), np.arange(n - 64, n)]))
     codes, _ = ofp8.cast(obf16.widen(bits[pos]), np.float32(s), fmt)
     assert np.array_equal(q[pos], codes)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_large_ragged_cast(bf16):
+    """A tensor past the size where the cast switches to its large-tensor
+    workgroup shape, with a ragged tail (not a whole number of pieces or
+    workgroups): amax and saturation count exact over everything, bytes exact on
+    a sample that includes both ends and every saturating element."""
+    n = (1 << 28) + 12345 + (3 if bf16 else 1)
+    print(f"[large ragged cast] bf16={bf16} n={n}", flush=True)
+    x = workloads.normal(n, 4242, 1.0)
+    x[np.random.default_rng(5).choice(n, 997, replace=False)] = 1000.0  # saturate at s = 1
+    scale = 1.0
+    if bf16:
+        bits = workloads.to_bf16_bits(x)
+        q, _, su, am, sat = run_cast(dev_bf16(bits), dsg.E4M3, scale)
+        get = lambda idx: obf16.widen(bits[idx])
+    else:
+        q, _, su, am, sat = run_cast(dev_f32(x), dsg.E4M3, scale)
+        get = lambda idx: x[idx]
+    assert su == scale
+    assert sat == 997
+    step = 1 << 24
+    amax_all = max(oamax.amax(get(np.arange(lo, min(lo + step, n)))) for lo in range(0, n, step))
+    assert am == f32_bits(amax_all)
+    rng = np.random.default_rng(7)
+    pos = np.unique(np.concatenate([rng.choice(n, 1 << 18, replace=False), np.arange(4096),
+                                    np.arange(n - 40000, n),
+                                    np.flatnonzero(x == 1000.0)]))
+    codes, _ = ofp8.cast(get(pos), np.float32(scale), dsg.E4M3)
+    assert np.array_equal(q[pos], codes)
