@@ -31,3 +31,16 @@ def test_scale_update_needs_a_format_per_tensor():
     with pytest.raises(ValueError, match="formats"):
         dsg.fp8ds_scale_update(h, torch.zeros(3, dtype=torch.int32), torch.zeros(3), [0, 0], 0, 0,
                                torch.ones(3))
+
+
+def test_mx_host_tensors_and_shapes_are_rejected():
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    q = torch.zeros(4, 64, dtype=torch.uint8)
+    s = torch.zeros(4, 2, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="CUDA"):
+        dsg.fp8ds_cast_mx(x, dsg.E4M3, q, s)
+    with pytest.raises(ValueError, match="2-D"):
+        dsg.fp8ds_cast_mx(x.view(-1), dsg.E4M3, q, s)
+    with pytest.raises(ValueError, match="CUDA"):
+        dsg.fp8ds_gemm_mx(4, 4, 128, q, dsg.E4M3, 128, s, 4, q, dsg.E4M3, 128, s, 4,
+                          torch.zeros(4, 4, dtype=torch.bfloat16), 4)

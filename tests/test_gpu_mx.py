@@ -303,3 +303,22 @@ def test_mx_linear_matches_the_raw_calls():
         dsg.fp8ds_gemm_mx(m, n, k, a[0], a[2], k, a[1], k // 32, b[0], b[2], k, b[1], k // 32, c, n)
         torch.cuda.synchronize()
         assert torch.equal(out[key].view(torch.int16), c.view(torch.int16)), key
+
+
+def test_mx_degenerate_shapes():
+    """K = 0 writes zeros (and amax 0); M = 0 only resets the output amax; an
+    empty cast is a no-op."""
+    c = torch.full((64, 64), 7.0, dtype=torch.float32, device=DEV)
+    am = torch.full((1,), 5.0, device=DEV)
+    u8 = torch.zeros(1, dtype=torch.uint8, device=DEV)
+    dsg.fp8ds_gemm_mx(64, 64, 0, u8, dsg.E4M3, 16, None, 4, u8, dsg.E4M3, 16, None, 4, c, 64, am)
+    torch.cuda.synchronize()
+    assert not c.any() and am.item() == 0.0
+    am.fill_(5.0)
+    dsg.fp8ds_gemm_mx(0, 64, 128, u8, dsg.E4M3, 128, u8, 4, u8, dsg.E4M3, 128, u8, 4, c, 64, am)
+    torch.cuda.synchronize()
+    assert am.item() == 0.0
+    x = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    dsg.fp8ds_cast_mx(x, dsg.E4M3, torch.zeros(0, dtype=torch.uint8, device=DEV),
+                      torch.zeros(0, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
