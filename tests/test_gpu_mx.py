@@ -315,7 +315,9 @@ def test_mx_degenerate_shapes():
     torch.cuda.synchronize()
     assert not c.any() and am.item() == 0.0
     am.fill_(5.0)
-    dsg.fp8ds_gemm_mx(0, 64, 128, u8, dsg.E4M3, 128, u8, 4, u8, dsg.E4M3, 128, u8, 4, c, 64, am)
+    b = torch.zeros(64, 128, dtype=torch.uint8, device=DEV)
+    sb = torch.full((64, 4), 127, dtype=torch.uint8, device=DEV)
+    dsg.fp8ds_gemm_mx(0, 64, 128, u8, dsg.E4M3, 128, u8, 4, b, dsg.E4M3, 128, sb, 4, c, 64, am)
     torch.cuda.synchronize()
     assert am.item() == 0.0
     x = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
