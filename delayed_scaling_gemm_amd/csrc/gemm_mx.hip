@@ -29,7 +29,7 @@ template <bool EXACT>
 static hipError_t launch_mx_path(const GemmProblem& q, int num_cus, hipStream_t stream) {
   if constexpr (EXACT) {
     const int64_t big_tiles = ((q.M + 255) / 256) * ((q.N + 255) / 256);
-    if (big_tiles >= num_cus) return launch_mx_tile<256, 256, EXACT>(q, stream);
+    if (big_tiles >= num_cus && q.K >= kBigTileMinK) return launch_mx_tile<256, 256, EXACT>(q, stream);
   }
   return launch_mx_tile<128, 128, EXACT>(q, stream);
 }
