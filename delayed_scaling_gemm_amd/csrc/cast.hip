@@ -199,9 +199,6 @@ __global__ __launch_bounds__(TH) void cast_kernel(CastArgs p) {
 #define FP8DS_TRANSPOSE_TILES 1
 #endif
 constexpr int kTransposeTiles = FP8DS_TRANSPOSE_TILES;
-#ifndef FP8DS_TRANSPOSE_UNROLL
-#define FP8DS_TRANSPOSE_UNROLL 4
-#endif
 
 template <bool BF16, int FMT, bool STATS>
 __global__ __launch_bounds__(256) void cast_transpose_kernel(
@@ -227,7 +224,20 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(
       // pieces of 16 input bytes (8 BF16 or 4 FP32 elements); pass i takes pieces
       // u = 256 (NP i + k) + tid of the tile, so a wave's loads cover whole row runs
       constexpr int PER = BF16 ? 8 : 4, NP = 16 / PER, PPR = T / PER;
-#pragma unroll FP8DS_TRANSPOSE_UNROLL
+      // all of the tile's loads are issued before the first conversion (loaded
+      // pass by pass, each pass waited for its own loads, and the tile paid the
+      // load latency once per pass)
+      u32x4 vin[4][NP];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const int u = 256 * (NP * i + k) + tid;
+          vin[i][k] = *reinterpret_cast<const u32x4*>(
+              static_cast<const char*>(xp) +
+              ((r0 + u / PPR) * cols + c0 + (u % PPR) * PER) * (BF16 ? 2 : 4));
+        }
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
         int rr[NP], cc[NP];
         int64_t off[NP];
@@ -238,8 +248,7 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(
           rr[k] = u / PPR;
           cc[k] = (u % PPR) * PER;
           off[k] = (r0 + rr[k]) * cols + c0 + cc[k];
-          const u32x4 w = *reinterpret_cast<const u32x4*>(
-              static_cast<const char*>(xp) + off[k] * (BF16 ? 2 : 4));
+          const u32x4 w = vin[i][k];
           d[4 * k] = w.x; d[4 * k + 1] = w.y; d[4 * k + 2] = w.z; d[4 * k + 3] = w.w;
         }
         if constexpr (BF16) {
