@@ -67,7 +67,7 @@ struct CastArgs {
 // (see block_commit).  Pieces whose group partners lie past the end, and the last
 // fewer-than-one-piece elements, go element by element.
 //
-// Workgroup shape (threads T, groups per thread G), measured on the box over
+// Workgroup shape (threads T, groups per thread G), measured on MI355X over
 // BF16 casts: 1024 x 4 (64 Ki elements per workgroup) is best on tensors of
 // tens of millions of elements, where it makes exactly two rounds of two
 // resident workgroups per CU on a 4096 x 16384 tensor; 256 x 8 (32 Ki) is 5-7%

@@ -1034,7 +1034,7 @@ static hipError_t launch_tile(const GemmProblem& q, hipStream_t s) {
 
 // Tile choice: 256 x 256 tiles when they alone give every CU at least one tile
 // and K is long enough to amortise their longer prologue and epilogue, else
-// 128 x 128 tiles (two resident per CU).  Measured on the box: with K <= 2048
+// 128 x 128 tiles (two resident per CU).  Measured on MI355X: with K <= 2048
 // the smaller tiles are 9-22% faster (512 x 256^3 batched: 52 -> 46 us;
 // 16384 x 4096 x 2048: 267 -> 243 us), from K = 4096 on the larger ones are
 // 3-10% faster.

@@ -1,6 +1,7 @@
 """bench.py's command line on the CPU: more than one GPU is refused with a
 message (the benchmark measures one GPU), and the traffic figures are read only
-while the kernel source matches the one the counters were taken on."""
+while the kernel's code (its comments aside) matches the code the counters were
+taken on."""
 
 import os
 import subprocess
@@ -25,3 +26,14 @@ def test_traffic_follows_the_kernel_source_hash(monkeypatch):
     assert t is None or t > 0
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "not-the-source")
     assert bench.measured_traffic("gemm_fwd_nt") is None
+
+
+def test_kernel_hash_sees_code_not_comments():
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = "int f(int x) {  // doubles x\n  /* body */\n  return 2 * x;\n}\n"
+    reworded = "// f: twice its argument\nint f(int x) {  // x times two\n\n  return 2 * x;   \n}\n"
+    changed = "int f(int x) {  // doubles x\n  return 3 * x;\n}\n"
+    assert bench._code_only(src) == bench._code_only(reworded)
+    assert bench._code_only(src) != bench._code_only(changed)
