@@ -455,10 +455,12 @@ __device__ __forceinline__ float dq(float a, float r, float c) {
   if constexpr (VS) return (a * r) * c;
   else return a * r;
 }
+// `stage0`, `stage1`: the two halves of the operand tiles' LDS (at least 2 WTM WTN
+// 2 bytes each), free once every wave has passed the epilogue's first barrier.
 template <int BM, int BN, int FM, int FN, int WTM, int WTN, bool VS = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM][FN], int64_t m0,
                                          int64_t n0, int wm, int wn, int tid, int64_t bz, float d,
-                                         uint32_t* red) {
+                                         uint32_t* red, uint8_t* stage0, uint8_t* stage1) {
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t M = p.M, N = p.N;
   const int64_t mb = m0 + wm * WTM + (lane & 31);
@@ -468,11 +470,23 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
   if (!p.out_f32) {
     uint16_t* C = static_cast<uint16_t*>(p.C) + bz * p.stride_c;
     if (full) {
+      // The wave's WTM x WTN block goes through LDS and leaves in whole row runs
+      // (CH lanes per row, 16 bytes each).  Stored straight from the accumulator
+      // layout, one instruction wrote 16 bytes into each of 32 rows; those stores
+      // cost ~12 us per round of 256 tiles of 256 x 256, about twice the time the
+      // output's HBM writes take.  Chunk c of staged row r sits at c ^ (r % CH).
+      constexpr int RB = WTN * 2;   // bytes per staged row
+      constexpr int CH = RB / 16;   // 16-byte chunks per row
+      constexpr int RPI = 64 / CH;  // rows per read-back instruction
+      static_assert(2 * WTM * RB <= BM * 2 * kRowBytes && 2 * WTM * RB <= BN * 2 * kRowBytes,
+                    "two waves' blocks fit in each half of the operand tiles' LDS");
+      uint8_t* st = (wave < 2 ? stage0 : stage1) + (wave & 1) * WTM * RB;
+      __syncthreads();  // every wave has finished reading the operand tiles
       u16x2_t am2 = {0, 0};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        uint16_t* row = C + (mb + i * 32) * p.ldc + nb;
         const float r = VS ? p.inv_a[mb + i * 32] : d;
+        const int sr = i * 32 + (lane & 31);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -483,11 +497,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
                                             dq<VS>(acc[i][j][4 * g + 1], r, c[1]));
             const uint32_t hi = pack_bf16x2(dq<VS>(acc[i][j][4 * g + 2], r, c[2]),
                                             dq<VS>(acc[i][j][4 * g + 3], r, c[3]));
-            *reinterpret_cast<u32x2*>(row + j * 32 + 8 * g) = u32x2{lo, hi};
+            const int ch = 4 * j + g;  // columns 32 j + 8 g + [0, 8) of the block
+            *reinterpret_cast<u32x2*>(st + sr * RB + ((ch ^ (sr % CH)) * 16) + 8 * (lane >> 5)) =
+                u32x2{lo, hi};
             am2 = __builtin_elementwise_max(am2, __builtin_elementwise_max(abs_bf16x2(lo), abs_bf16x2(hi)));
           }
       }
       amax = (uint32_t)max(am2[0], am2[1]) << 16;
+      __syncthreads();  // the block is staged
+      const int ch = lane % CH;
+      uint16_t* out = C + (m0 + wm * WTM) * p.ldc + n0 + wn * WTN + ch * 8;
+#pragma unroll
+      for (int it = 0; it < WTM / RPI; ++it) {
+        const int sr = it * RPI + lane / CH;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + sr * RB + ((ch ^ (sr % CH)) * 16));
+        *reinterpret_cast<u32x4*>(out + sr * p.ldc) = v;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -969,7 +994,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     if (nk > 0) stage(nk - 1, std::false_type{});
   }
 
-  epilogue<BM, BN, FM, FN, WTM, WTN, VS>(p, acc, m0, n0, wm, wn, tid, bz, d, red);
+  epilogue<BM, BN, FM, FN, WTM, WTN, VS>(p, acc, m0, n0, wm, wn, tid, bz, d, red,
+                                        reinterpret_cast<uint8_t*>(lds_a),
+                                        reinterpret_cast<uint8_t*>(lds_b));
 }
 
 // ------------------------------------------------------------------ dispatch
