@@ -161,11 +161,10 @@ int fp8ds_cast_batched(const void* x, fp8ds_dtype xt, int64_t batch, int64_t n, 
       return fail(FP8DS_ERR_ALIGN, "fp8ds_cast_batched: operands and strides must keep 16-byte "
                                    "alignment");
   }
-  hipError_t e = fp8ds::launch_prologue(batch, scale, scale_used, amax, sat_count, stream);
-  if (e == hipSuccess && n > 0)
-    e = fp8ds::launch_cast(x, xt == FP8DS_BF16, batch, n, stride_x, (int)fmt, scale, q, stride_q,
-                           amax, sat_count, nullptr, num_cus(), stream);
-  return hip_status(e, "fp8ds_cast_batched");
+  return hip_status(fp8ds::launch_cast_batched(x, xt == FP8DS_BF16, batch, n, stride_x, (int)fmt,
+                                               scale, q, stride_q, scale_used, amax, sat_count,
+                                               stream),
+                    "fp8ds_cast_batched");
 }
 
 int fp8ds_scale_update(int n_tensors, int hist_len, float* history, int32_t* cursor,

@@ -49,6 +49,9 @@ struct CastArgs {
   uint32_t* amax;     // [batch] or null
   unsigned long long* sat;  // [batch] or null
   unsigned long long* health;  // [batch][4] NaN, Inf, zero, near-max counts (STATS)
+  float* scale_used;  // [batch] or null: written only with `direct`
+  int direct;         // one workgroup per tensor: it stores amax, saturation count
+                      // and the scale snapshot itself (no prologue kernel)
 };
 
 // Each workgroup of T threads owns the contiguous range of T * kGroups * 16
@@ -122,6 +125,7 @@ __global__ __launch_bounds__(TH) void cast_kernel(CastArgs p) {
   Health h;
   const int b = blockIdx.y;
   const float s = WRITE_Q ? p.scale[b] : 1.0f;
+  if (WRITE_Q && p.direct && p.scale_used && threadIdx.x == 0) p.scale_used[b] = s;
   const bool want_sat = WRITE_Q && p.sat != nullptr;
   const int64_t n = p.n;
   const int64_t npieces = n / PER;
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(TH) void cast_kernel(CastArgs p) {
     cast1<BF16, FMT, WRITE_Q, STATS>(x, q, t0 + threadIdx.x, s, amax, sat, want_sat, h);
   if constexpr (BF16) amax = max(amax, ((uint32_t)max(amax2.x, amax2.y)) << 16);
   block_commit<STATS>(amax, sat, h, p.amax ? p.amax + b : nullptr, want_sat ? p.sat + b : nullptr,
-                      STATS ? p.health + 4 * b : nullptr, red);
+                      STATS ? p.health + 4 * b : nullptr, red, p.direct != 0);
 }
 
 // ------------------------------------------------------------------ cast + transposed copy
@@ -335,6 +339,7 @@ static hipError_t launch_cast_shape(const CastArgs& a, int64_t batch, hipStream_
   const int64_t pieces = a.n / CG::kPer;
   int64_t gx = (pieces + per_block - 1) / per_block;
   if (gx < 1) gx = 1;  // block 0 also takes the ragged tail (fewer than one piece)
+  if (a.direct && gx != 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL((cast_kernel<BF16, FMT, WRITE_Q, STATS, TH, GR>),
                      dim3((unsigned)gx, (unsigned)batch), dim3((unsigned)CG::kThreads), 0, stream,
                      a);
@@ -372,6 +377,32 @@ hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64
                 : launch_cast_f<false, true>(a, fmt, batch, stream);
   return bf16 ? launch_cast_f<true, false>(a, fmt, batch, stream)
               : launch_cast_f<false, false>(a, fmt, batch, stream);
+}
+
+// Batched casts of tensors that one workgroup of the 1024 x 4 shape covers
+// (64 Ki elements, e.g. 256 x 256) need no cross-workgroup reduction: that
+// workgroup stores the tensor's amax and saturation count and snapshots its
+// scale, and the prologue kernel (with its launch gap) is not needed.  Larger
+// tensors take the prologue and the atomic reductions.
+constexpr int64_t kOneBlockElems = 1024 * 4 * 16;
+static_assert(kOneBlockElems < kCastLargeElems, "such tensors take the 1024 x 4 shape");
+
+hipError_t launch_cast_batched(const void* x, bool bf16, int64_t batch, int64_t n,
+                               int64_t stride_x, int fmt, const float* scale, uint8_t* q,
+                               int64_t stride_q, float* scale_used, float* amax, uint64_t* sat,
+                               hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  if (n > 0 && n <= kOneBlockElems) {
+    CastArgs a{x, n, stride_x, scale, q, stride_q, reinterpret_cast<uint32_t*>(amax),
+               reinterpret_cast<unsigned long long*>(sat), nullptr, scale_used, 1};
+    return bf16 ? launch_cast_f<true, false>(a, fmt, batch, stream)
+                : launch_cast_f<false, false>(a, fmt, batch, stream);
+  }
+  hipError_t e = launch_prologue(batch, scale, scale_used, amax, sat, stream);
+  if (e == hipSuccess && n > 0)
+    e = launch_cast(x, bf16, batch, n, stride_x, fmt, scale, q, stride_q, amax, sat, nullptr, 0,
+                    stream);
+  return e;
 }
 
 template <bool BF16, int FMT, bool STATS>

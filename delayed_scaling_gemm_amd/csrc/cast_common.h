@@ -223,11 +223,14 @@ __device__ __forceinline__ u32x4 cast16_f32(const uint32_t (&d)[16], float s, ui
 // per wave and quantity, then wave 0 reduces across the waves in parallel (lane
 // w takes wave w's words) and issues at most one atomic per quantity.  The amax
 // atomic is skipped when the global value already covers the workgroup's: it
-// only grows, and a stale read only costs an extra atomic.
+// only grows, and a stale read only costs an extra atomic.  `direct`: the
+// workgroup is the only one of its tensor, and stores the results instead (the
+// outputs need no zeroing beforehand).
 template <bool STATS>
 __device__ __forceinline__ void block_commit(uint32_t amax_bits, uint32_t sat, const Health& h,
                                              uint32_t* g_amax, unsigned long long* g_sat,
-                                             unsigned long long* g_health, uint32_t* smem) {
+                                             unsigned long long* g_health, uint32_t* smem,
+                                             bool direct = false) {
   constexpr int NQ = STATS ? 6 : 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   uint32_t v[NQ];
@@ -250,7 +253,14 @@ __device__ __forceinline__ void block_commit(uint32_t amax_bits, uint32_t sat, c
     t[0] = wave_max_u32(t[0]);
 #pragma unroll
     for (int k = 1; k < NQ; ++k) t[k] = wave_sum_u32(t[k]);
-    if (lane == 0) {
+    if (lane == 0 && direct) {
+      if (g_amax) *g_amax = canonical_amax_bits(t[0]);
+      if (g_sat) *g_sat = (unsigned long long)t[1];
+      if constexpr (STATS) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) g_health[k] = (unsigned long long)t[2 + k];
+      }
+    } else if (lane == 0) {
       if (g_amax) {
         const uint32_t mb = canonical_amax_bits(t[0]);
         if (mb > __hip_atomic_load(g_amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))

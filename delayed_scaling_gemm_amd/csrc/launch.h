@@ -19,6 +19,13 @@ hipError_t launch_prologue(int64_t count, const float* scale, float* scale_used,
 hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride_x,
                        int fmt, const float* scale, uint8_t* q, int64_t stride_q, float* amax,
                        uint64_t* sat, uint64_t* health, int num_cus, hipStream_t stream);
+// Batched cast with its output resets and scale snapshot (scale_used, amax, sat:
+// [batch] or null), taken by the cast kernel itself where one workgroup covers a
+// tensor, else by the prologue kernel.
+hipError_t launch_cast_batched(const void* x, bool bf16, int64_t batch, int64_t n,
+                               int64_t stride_x, int fmt, const float* scale, uint8_t* q,
+                               int64_t stride_q, float* scale_used, float* amax, uint64_t* sat,
+                               hipStream_t stream);
 
 // Cast of a [rows x cols] tensor writing q and its transpose qt (health as above).
 hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,

@@ -189,6 +189,46 @@ def test_cast_batched():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n", [65536, 65531, 65537, 70000])
+def test_cast_batched_one_workgroup_boundary(fmt, n):
+    """Batched bf16 casts on both sides of 64 Ki elements per tensor: up to it one
+    workgroup covers a tensor and stores amax, saturation count and the scale
+    snapshot itself; beyond it the outputs are reset by a prologue and reduced
+    atomically.  The outputs start as garbage and the call runs twice: nothing
+    may carry over.  Tensors hold NaN, Inf and saturating values."""
+    rng = np.random.default_rng(n + fmt)
+    B = 5
+    stride = (n + 15) // 16 * 16
+    x32 = (rng.standard_normal((B, n)) * rng.uniform(0.1, 100, (B, 1))).astype(np.float32)
+    x32[1, n // 3] = np.inf
+    x32[2, 7] = np.nan
+    x32[3, n - 1] = -1e6  # saturates at any scale here
+    bits = obf16.round_to_bf16_vec(x32.astype(np.float64)).reshape(B, n)
+    xw = obf16.widen(bits.ravel()).reshape(B, n)
+    xp = np.zeros((B, stride), dtype=np.uint16)
+    xp[:, :n] = bits
+    xd = dev_bf16(xp)
+    scales = np.array([1.0, 448 / 3.3, 2.0**-3, 5.0, 1e-3], np.float32)
+    s = dev_f32(scales)
+    q = torch.full((B, stride), 0xAB, dtype=torch.uint8, device=DEV)
+    su = torch.full((B,), -7.0, dtype=torch.float32, device=DEV)
+    am = torch.full((B,), 12345.0, dtype=torch.float32, device=DEV)
+    sat = torch.full((B,), 999, dtype=torch.int64, device=DEV)
+    L = dsg.lib()
+    for _ in range(2):
+        dsg._check(L.fp8ds_cast_batched(xd.data_ptr(), dsg.BF16, B, n, stride, fmt, s.data_ptr(),
+                                        q.data_ptr(), stride, su.data_ptr(), am.data_ptr(),
+                                        sat.data_ptr(), dsg._stream(None)))
+    torch.cuda.synchronize()
+    qn, amn, satn = q.cpu().numpy(), am.cpu().numpy().view(np.uint32), sat.cpu().numpy()
+    for b in range(B):
+        codes, oa, osat = oracle_cast(xw[b], fmt, scales[b])
+        assert np.array_equal(qn[b, :n], codes), b
+        assert amn[b] == oa and satn[b] == osat, (b, hex(amn[b]), hex(oa), satn[b], osat)
+    assert np.array_equal(su.cpu().numpy(), scales)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_stress_tensor_full_size(fmt):
     """The bandwidth-stress workload at its full size (2^30 bf16 elements): amax and
     saturation count exact over the whole tensor, bytes exact on a sample that
