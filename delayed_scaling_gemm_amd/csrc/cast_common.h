@@ -72,6 +72,19 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
   return nan ? encode4_sw<FMT>(a, b, c, d) : encode4_hw<FMT>(a, b, c, d);
 }
 
+// Codes of one piece whose scaled values are not NaN (finite inputs and a
+// finite scale): the packed converts alone, no NaN test.
+template <bool BF16, int FMT>
+__device__ __forceinline__ u32x2 piece_codes_finite(const u32x4& d, float s) {
+  if constexpr (BF16) {
+    return u32x2{encode4_hw<FMT>(bf16_lo(d.x) * s, bf16_hi(d.x) * s, bf16_lo(d.y) * s, bf16_hi(d.y) * s),
+                 encode4_hw<FMT>(bf16_lo(d.z) * s, bf16_hi(d.z) * s, bf16_lo(d.w) * s, bf16_hi(d.w) * s)};
+  } else {
+    return u32x2{encode4_hw<FMT>(__uint_as_float(d.x) * s, __uint_as_float(d.y) * s,
+                                 __uint_as_float(d.z) * s, __uint_as_float(d.w) * s), 0u};
+  }
+}
+
 // Codes of one piece: 8 bytes (BF16, returned in .x/.y) or 4 bytes (FP32, in .x).
 template <bool BF16, int FMT>
 __device__ __forceinline__ u32x2 piece_codes(const u32x4& d, float s) {

@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256) void mx_cast_kernel(const void* __restrict__ x
       u32x2 c;
       if (code == 255u) {
         c = u32x2{0x7F7F7F7Fu, BF16 ? 0x7F7F7F7Fu : 0u};
-      } else {
-        c = piece_codes<BF16, FMT>(v[j], __uint_as_float((254u - code) << 23));
+      } else {  // the block's amax is finite: so is every value in it
+        c = piece_codes_finite<BF16, FMT>(v[j], __uint_as_float((254u - code) << 23));
       }
       if constexpr (BF16)
         __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q) + pc);
@@ -87,29 +87,26 @@ __global__ __launch_bounds__(256) void mx_cast_kernel(const void* __restrict__ x
 // (shuffles), then over the four waves through LDS.  Column codes are parked in
 // an LDS tile and written transposed by tile_store_qt.  Whole tiles only.
 
-// Codes of one piece with one multiplier per element (column); columns whose
-// block holds NaN or Inf (code 255) get the NaN code.
+// Codes of one piece with one multiplier per element (column).  Columns whose
+// block holds NaN or Inf (scale code 255) get the NaN code: `nan_bytes` has
+// 0xFF in their bytes.  Every other column's block has a finite amax, so its
+// values are finite and the packed converts alone encode them; whatever they
+// give for a NaN column's bytes is replaced.
 template <bool BF16, int FMT>
 __device__ __forceinline__ u32x2 piece_codes_cols(const u32x4& d, const float (&m)[8],
-                                                  const uint32_t (&code)[8]) {
+                                                  const uint32_t (&nan_bytes)[2]) {
   u32x2 c;
   if constexpr (BF16) {
-    c = u32x2{encode4<FMT>(bf16_lo(d.x) * m[0], bf16_hi(d.x) * m[1], bf16_lo(d.y) * m[2],
-                           bf16_hi(d.y) * m[3]),
-              encode4<FMT>(bf16_lo(d.z) * m[4], bf16_hi(d.z) * m[5], bf16_lo(d.w) * m[6],
-                           bf16_hi(d.w) * m[7])};
+    c = u32x2{encode4_hw<FMT>(bf16_lo(d.x) * m[0], bf16_hi(d.x) * m[1], bf16_lo(d.y) * m[2],
+                              bf16_hi(d.y) * m[3]),
+              encode4_hw<FMT>(bf16_lo(d.z) * m[4], bf16_hi(d.z) * m[5], bf16_lo(d.w) * m[6],
+                              bf16_hi(d.w) * m[7])};
   } else {
-    c = u32x2{encode4<FMT>(__uint_as_float(d.x) * m[0], __uint_as_float(d.y) * m[1],
-                           __uint_as_float(d.z) * m[2], __uint_as_float(d.w) * m[3]), 0u};
+    c = u32x2{encode4_hw<FMT>(__uint_as_float(d.x) * m[0], __uint_as_float(d.y) * m[1],
+                              __uint_as_float(d.z) * m[2], __uint_as_float(d.w) * m[3]), 0u};
   }
-  constexpr int PER = BF16 ? 8 : 4;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    if (code[e] == 255u) {
-      const uint32_t sh = 8u * (e & 3);
-      c[e >> 2] = (c[e >> 2] & ~(0xFFu << sh)) | (0x7Fu << sh);
-    }
-  }
+  for (int k = 0; k < 2; ++k) c[k] = (c[k] & ~nan_bytes[k]) | (0x7F7F7F7Fu & nan_bytes[k]);
   return c;
 }
 
@@ -184,7 +181,7 @@ __global__ __launch_bounds__(256) void mx_cast_transpose_kernel(
       if (code == 255u)
         c = u32x2{0x7F7F7F7Fu, BF16 ? 0x7F7F7F7Fu : 0u};
       else
-        c = piece_codes<BF16, FMT>(v[k], __uint_as_float((254u - code) << 23));
+        c = piece_codes_finite<BF16, FMT>(v[k], __uint_as_float((254u - code) << 23));
       const int64_t off = (r0 + rr[k]) * cols + c0 + cc;
       if constexpr (BF16)
         *reinterpret_cast<u32x2*>(q + off) = c;
@@ -207,9 +204,13 @@ __global__ __launch_bounds__(256) void mx_cast_transpose_kernel(
 #pragma unroll
       for (int e = 4; e < 8; ++e) { ccode[e] = 0u; m[e] = 1.0f; }
     }
+    uint32_t nan_bytes[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (ccode[e] == 255u) nan_bytes[e >> 2] |= 0xFFu << (8 * (e & 3));
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
-      const u32x2 c = piece_codes_cols<BF16, FMT>(v[k], m, ccode);
+      const u32x2 c = piece_codes_cols<BF16, FMT>(v[k], m, nan_bytes);
       if constexpr (BF16)
         tile_park8(tile, rr[k], cc, c);
       else
