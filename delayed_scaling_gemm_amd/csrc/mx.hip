@@ -135,7 +135,9 @@ __global__ __launch_bounds__(256) void mx_cast_transpose_kernel(
   constexpr int PPR = T / PER;        // pieces per tile row
   constexpr int PPB = 32 / PER;       // pieces per row block
   __shared__ __attribute__((aligned(16))) uint8_t tile[T * T];
-  __shared__ uint32_t red[2][4][PPR][PER];
+  // column amax exchange; rows padded to PER + 1 words so that the lanes' stores
+  // and reads of one element fall in different LDS banks
+  __shared__ uint32_t red[2][4][PPR][PER + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * T, r0 = (int64_t)blockIdx.y * T;
   const int cc = (tid % PPR) * PER;  // this thread's columns in the tile
