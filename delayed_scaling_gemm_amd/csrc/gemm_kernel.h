@@ -317,6 +317,13 @@ struct LoaderSel<false, ROWS, NT, KB, WIDEN, FMT> {
 // own, and a workgroup barrier's fence only waits for LDS operations.
 // (s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt unconstrained.)
 __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N vector memory instructions of this wave are outstanding
+// (they complete in issue order): vmcnt in bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void vmem_wait_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 template <int ROWS, int NT>
 struct LoaderKCDirect {
@@ -391,6 +398,13 @@ struct LoaderMNDirect {
     }
   }
 };
+
+// Direct-load instructions one wave issues for one operand's stage.
+template <bool KC, int ROWS, int NT>
+constexpr int direct_issues() {
+  if constexpr (KC) return LoaderKCDirect<ROWS, NT>::kPerWave;
+  else return LoaderMNDirect<ROWS, NT>::kPerWave;
+}
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b8).  Within each group of 16
 // lanes, lane i receives byte (i % 8) of the 8-byte pieces addressed by lanes
@@ -795,8 +809,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       if constexpr (DIRECT) {
         load_scales(0);
         issue_direct(0, 0);
-        if (nk > 1) issue_direct(1, 1);
-        vmem_wait_all();
+        if (nk > 1) {
+          // stage 0 (and everything before it) complete, stage 1 still in flight
+          issue_direct(1, 1);
+          vmem_wait_n<direct_issues<A_KC, BM, NT>() + direct_issues<B_KC, BN, NT>()>();
+        } else {
+          vmem_wait_all();
+        }
       } else {
         la.load(A, p.lda, m0, M, 0, K, tid);
         lb.load(B, p.ldb, n0, N, 0, K, tid);
@@ -949,8 +968,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       if constexpr (DIRECT) {
         load_scales8(0);
         issue_direct(0, 0);
-        if (nk > 1) issue_direct(1, 1);
-        vmem_wait_all();
+        if (nk > 1) {
+          issue_direct(1, 1);
+          vmem_wait_n<direct_issues<A_KC, BM, NT>() + direct_issues<B_KC, BN, NT>()>();
+        } else {
+          vmem_wait_all();
+        }
       } else {
         la.load(A, p.lda, m0, M, 0, K, tid);
         lb.load(B, p.ldb, n0, N, 0, K, tid);
