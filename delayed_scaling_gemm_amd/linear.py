@@ -42,7 +42,10 @@ class DelayedScalingLinear:
 
     def __init__(self, hist_len: int = 16, algo: int = ALGO_MAX, margin: int = 0,
                  fmts=(E4M3, E4M3, E5M2), device="cuda", health: bool = False,
-                 health_every: int = 1):
+                 health_every: int = 1, mma_fwd: int = MMA_EXACT, mma_bwd: int = MMA_EXACT):
+        # GEMM datapaths (fp8ds_mma) of the forward and of the two backward products
+        self.mma_fwd = mma_fwd
+        self.mma_bwd = mma_bwd
         self.health = health
         # the counting cast costs ~30% more than the plain one on large tensors:
         # run it on every `health_every`-th step only (the pages check every 100)
@@ -160,7 +163,7 @@ class DelayedScalingLinear:
         self._w_prepared = None
         # Y[M, N] = Xq[M, K] . Wq[K, N], with Wq^T stored [N, K] -> op T
         fp8ds_gemm(OP_N, OP_T, M, N, K, xq, self.fmts[X], K, su[X:X + 1], wqt, self.fmts[W], K,
-                   su[W:W + 1], y, N, self.amax_y, stream)
+                   su[W:W + 1], y, N, self.amax_y, stream, mma=self.mma_fwd)
         out = {"xq": xq, "wq": wq, "wqt": wqt, "y": y}
         n_upd = 2
         if dy is not None:
@@ -171,10 +174,10 @@ class DelayedScalingLinear:
             self._cast(DY, dy, dyq, None, stream)
             # dX[M, K] = dYq[M, N] . Wq^T   (Wq stored [K, N] = [N' x K'] -> op T)
             fp8ds_gemm(OP_N, OP_T, M, K, N, dyq, self.fmts[DY], N, su[DY:DY + 1], wq, self.fmts[W],
-                       N, su[W:W + 1], dx, K, None, stream)
+                       N, su[W:W + 1], dx, K, None, stream, mma=self.mma_bwd)
             # dW[K, N] = Xq^T . dYq         (Xq stored [M, K] = [K' x M'] -> op T)
             fp8ds_gemm(OP_T, OP_N, K, N, M, xq, self.fmts[X], K, su[X:X + 1], dyq, self.fmts[DY],
-                       N, su[DY:DY + 1], dw, N, self.amax_dw, stream)
+                       N, su[DY:DY + 1], dw, N, self.amax_dw, stream, mma=self.mma_bwd)
             out.update(dyq=dyq, dx=dx, dw=dw)
             n_upd = 3
         fp8ds_scale_update(self.history[:n_upd], self.cursor[:n_upd], am[:n_upd],

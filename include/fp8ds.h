@@ -166,6 +166,11 @@ int fp8ds_cast_health(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols,
 /*
  * fp8ds_cast_batched -- `batch` independent casts of equal size n, each with its
  * own scale (the per-problem scales of a batch of small Linears).
+ * [P3] §适用场景 (among the cases to treat with care: many small matrices) and
+ * §常见误区 误区一 (small matrices, frequent casts and scale kernels can eat the FP8
+ * gain): one launch casts every tensor of the batch, so a small matrix's cast
+ * costs no launch of its own.  Each tensor's cast is the scaled saturating cast
+ * of fp8ds_cast ([P2] §四 "动态缩放", the quantize step).
  *
  *   x          device, batch tensors of n elements, tensor b at x + b*stride_x elements
  *              (stride_x >= n, stride_x*elem_size a multiple of 16).
@@ -242,6 +247,10 @@ int fp8ds_gemm(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K,
 /*
  * fp8ds_gemm_batched -- `batch` independent GEMMs of one shape, each with its own
  * scales and output amax (many small Linears in one launch).
+ * [P3] §适用场景 (many small matrices among the cases to treat with care) and
+ * §常见误区 误区一 (small matrices can cancel the FP8 gain): the products of a
+ * batch of small Linears share one launch, one workgroup per output tile of any
+ * problem.  Each product is fp8ds_gemm's ([P2] §五).
  * Problem b uses A + b*stride_a, B + b*stride_b (bytes), C + b*stride_c (elements),
  * scale_a[b], scale_b[b], amax_c[b]; otherwise as fp8ds_gemm.  Strides must keep
  * every operand 16-byte aligned.

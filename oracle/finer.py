@@ -23,11 +23,14 @@ Readings:
   NaN).  Per-channel scaling of a weight W [K, N] (a scale per output channel n)
   is per-row scaling of its transpose [N, K]; per-token scaling of X [M, K] is
   per-row scaling of X.
-* The inverse scales are ``fl32(1 / s)``, one correctly rounded fp32 division.
-* GEMM with scale vectors: ``y[i, j] = bf16(acc[i, j] * ia[i] * ib[j])`` with
-  ``acc`` the exact sum of products of the decoded codes and ``ia``, ``ib`` the
-  inverse scales of the rows of op(A) and the columns of op(B); the product is
-  taken in fp64 here (exact for these operands up to the final rounding).
+* The inverse scales ``fl32(1 / s)`` are what a cast hands to a GEMM kernel
+  that multiplies; the oracle does not use them for the dequant.
+* GEMM with scale vectors: the pages' fp8 linear op divides the FP32 product by
+  the product of the two scales ([P2] §五); with one scale per row of op(A) and
+  per column of op(B) that is ``y[i, j] = bf16(acc[i, j] / fl32(s_a[i] * s_b[j]))``,
+  ``acc`` the exact sum of products of the decoded codes, the scale product one
+  fp32 multiply (as the per-tensor dequant of :mod:`oracle.gemm`), the division
+  in fp64 and one rounding to BF16.
 """
 
 from __future__ import annotations
@@ -73,10 +76,11 @@ def rowwise_cast(x: np.ndarray, fmt: int, margin: int):
     return codes, scale, sinv, amax
 
 
-def dequant_vec_to_bf16(acc: np.ndarray, inv_a: np.ndarray, inv_b: np.ndarray) -> np.ndarray:
-    """``bf16(acc[i, j] * ia[i] * ib[j])`` as uint16 bits (fp64 product, one bf16
-    rounding)."""
-    ia = np.asarray(inv_a, dtype=np.float32).astype(np.float64)
-    ib = np.asarray(inv_b, dtype=np.float32).astype(np.float64)
-    y = np.asarray(acc, dtype=np.float64) * ia[:, None] * ib[None, :]
+def dequant_vec_to_bf16(acc: np.ndarray, scale_a: np.ndarray, scale_b: np.ndarray) -> np.ndarray:
+    """``bf16(acc[i, j] / fl32(s_a[i] * s_b[j]))`` as uint16 bits (the scale product
+    one fp32 multiply, the division in fp64, one bf16 rounding)."""
+    sa = np.asarray(scale_a, dtype=np.float32)
+    sb = np.asarray(scale_b, dtype=np.float32)
+    prod = (sa[:, None] * sb[None, :]).astype(np.float32)  # fl32 of each pair
+    y = np.asarray(acc, dtype=np.float64) / prod.astype(np.float64)
     return bf16.round_to_bf16_vec(y)

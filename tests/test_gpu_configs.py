@@ -27,7 +27,7 @@ from oracle import bf16 as obf16  # noqa: E402
 from oracle import fp8 as ofp8  # noqa: E402
 from oracle import gemm as ogemm  # noqa: E402
 from oracle.scaling import ScalingState  # noqa: E402
-from tests.parity import bf16_bits, check_bf16_out, f32_bits  # noqa: E402
+from tests.parity import band_rows, bf16_bits, check_bf16_out, f32_bits  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -86,7 +86,7 @@ def test_forward_linear_4096_history_1024():
             assert lin.sat[i].item() == ofp8.saturation_count(obf16.widen(bits), st.scale, st.fmt)
         xq, wq = out["xq"].cpu().numpy(), out["wq"].cpu().numpy()
         assert np.array_equal(out["wqt"].cpu().numpy(), wq.T)
-        rows = np.sort(rng.choice(xb.shape[0], 48, replace=False))
+        rows = band_rows(xb.shape[0])
         check_gemm_rows(out["y"], xq, dsg.E4M3, dsg.OP_N, wq, dsg.E4M3, dsg.OP_N,
                         states["x"].scale, states["w"].scale, rows, f"y step {step}")
         yb = bf16_bits(out["y"])
@@ -133,8 +133,8 @@ def test_decoder_layer_projections_10_steps():
                 if a == dsg.ALGO_MAX and step in (0, 6, 9):
                     xq, wq, dyq = (out[k].cpu().numpy() for k in ("xq", "wq", "dyq"))
                     sx, sw, sdy = st["x"].scale, st["w"].scale, st["dy"].scale
-                    rm = np.sort(rng.choice(M, 12, replace=False))
-                    rk = np.sort(rng.choice(wb.shape[0], 12, replace=False))
+                    rm = band_rows(M)
+                    rk = band_rows(wb.shape[0])
                     check_gemm_rows(out["y"], xq, 0, 0, wq, 0, 0, sx, sw, rm, f"y {p} {step}")
                     check_gemm_rows(out["dx"], dyq, 1, 0, wq, 0, 1, sdy, sw, rm,
                                     f"dx {p} {step}")

@@ -100,8 +100,10 @@ def _run_rowcol(opa, opb, a_st, fa, b_st, fb, M, N, K, ia, ib, out=torch.bfloat1
 
 
 def _scales(rng, n):
-    """Inverse scales spanning several binades, not powers of two."""
-    return (rng.uniform(0.5, 2.0, n) * 2.0 ** rng.integers(-8, 9, n)).astype(np.float32)
+    """Scales spanning several binades, not powers of two, and the inverse scales
+    fl32(1 / s) a cast hands to the GEMM."""
+    s = (rng.uniform(0.5, 2.0, n) * 2.0 ** rng.integers(-8, 9, n)).astype(np.float32)
+    return s, np.array([ofin.inv_scale(v) for v in s], np.float32)
 
 
 @pytest.mark.parametrize("opa,opb", [(dsg.OP_N, dsg.OP_T), (dsg.OP_N, dsg.OP_N),
@@ -112,10 +114,10 @@ def test_rowcol_gemm_matches_oracle(opa, opb, fa, fb, M, N, K):
     rng = np.random.default_rng(M + N + K + 10 * opa + opb)
     a_st = finite_codes(rng, stored_shape(opa, M, K), fa)
     b_st = finite_codes(rng, stored_shape(opb, K, N), fb)
-    ia, ib = _scales(rng, M), _scales(rng, N)
+    (sa, ia), (sb, ib) = _scales(rng, M), _scales(rng, N)
     y, amax = _run_rowcol(opa, opb, a_st, fa, b_st, fb, M, N, K, ia, ib)
     acc, sum_abs = ogemm.gemm_exact(a_st, fa, opa, b_st, fb, opb)
-    ref = ofin.dequant_vec_to_bf16(acc, ia, ib)
+    ref = ofin.dequant_vec_to_bf16(acc, sa, sb)
     yg = obf16.widen(bf16_bits(y)).astype(np.float64)
     yr = obf16.widen(ref).astype(np.float64)
     fac = ia.astype(np.float64)[:, None] * ib.astype(np.float64)[None, :]
@@ -130,7 +132,7 @@ def test_rowcol_fp32_output(M, N, K):
     rng = np.random.default_rng(M * N)
     a_st = finite_codes(rng, (M, K), dsg.E4M3)
     b_st = finite_codes(rng, (N, K), dsg.E4M3)
-    ia, ib = _scales(rng, M), _scales(rng, N)
+    (_, ia), (_, ib) = _scales(rng, M), _scales(rng, N)
     y, _ = _run_rowcol(dsg.OP_N, dsg.OP_T, a_st, dsg.E4M3, b_st, dsg.E4M3, M, N, K, ia, ib,
                        out=torch.float32)
     acc, sum_abs = ogemm.gemm_exact(a_st, dsg.E4M3, dsg.OP_N, b_st, dsg.E4M3, dsg.OP_T)
@@ -181,13 +183,13 @@ def test_per_token_per_channel_forward_full_size_sampled():
     torch.cuda.synchronize()
     rows = np.random.default_rng(0).choice(M, 48, replace=False)
     xw = obf16.widen(xb[rows]).reshape(48, K)
-    codes_x, _, sinv_x, _ = ofin.rowwise_cast(xw, dsg.E4M3, 0)
-    codes_w, _, sinv_w, _ = ofin.rowwise_cast(obf16.widen(wb.T.copy()).reshape(N, K), dsg.E4M3, 0)
+    codes_x, s_x, sinv_x, _ = ofin.rowwise_cast(xw, dsg.E4M3, 0)
+    codes_w, s_w, sinv_w, _ = ofin.rowwise_cast(obf16.widen(wb.T.copy()).reshape(N, K), dsg.E4M3, 0)
     np.testing.assert_array_equal(xq.cpu().numpy()[rows], codes_x)
     np.testing.assert_array_equal(wq.cpu().numpy(), codes_w)
     np.testing.assert_array_equal(_bits(six.cpu().numpy()[rows]), _bits(sinv_x))
     acc, sum_abs = ogemm.gemm_exact(codes_x, dsg.E4M3, dsg.OP_N, codes_w, dsg.E4M3, dsg.OP_T)
-    ref = obf16.widen(ofin.dequant_vec_to_bf16(acc, sinv_x, sinv_w)).astype(np.float64)
+    ref = obf16.widen(ofin.dequant_vec_to_bf16(acc, s_x, s_w)).astype(np.float64)
     yg = obf16.widen(bf16_bits(y)[rows]).astype(np.float64)
     fac = sinv_x.astype(np.float64)[:, None] * sinv_w.astype(np.float64)[None, :]
     assert (np.abs(yg - ref) <= bf16_ulp(ref) + ACC_REL * fac * sum_abs).all()

@@ -16,7 +16,7 @@ from oracle import fp8 as ofp8  # noqa: E402
 from oracle import gemm as ogemm  # noqa: E402
 from oracle import linear as olinear  # noqa: E402
 from oracle.scaling import ScalingState  # noqa: E402
-from tests.parity import bf16_bits, check_bf16_out, f32_bits  # noqa: E402
+from tests.parity import band_rows, bf16_bits, check_bf16_out, f32_bits  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -107,7 +107,8 @@ def _sampled_rows_check(gpu_out, a_codes, fa, opa, b_codes, fb, opb, sa, sb, row
 def test_fwd_bwd_4096_full_size_sampled():
     """The M=16384, 4096-hidden Linear at full size, launched exactly as the
     benchmark launches it: all cast bytes on a sample, amax and saturation exact,
-    64 sampled rows of each GEMM output against the oracle, output amax exact."""
+    rows of each GEMM output against the oracle (first, last and one moving row of
+    every 256-row tile band), output amax exact."""
     xb, wb, dyb = workloads.fwd_bwd_4096()
     print("[fwd_bwd_4096] inputs ready", flush=True)
     lin = DelayedScalingLinear(hist_len=16)
@@ -127,10 +128,10 @@ def test_fwd_bwd_4096_full_size_sampled():
         i_x, i_w, i_dy = 0, 1, 2
         su = lin.scale_used.cpu().numpy()
         assert f32_bits(su[i_x]) == f32_bits(states["x"].scale)
-        rows = np.sort(rng.choice(16384, 64, replace=False))
+        rows = band_rows(16384)
         _sampled_rows_check(out["y"], xq, 0, 0, wq, 0, 0, su[i_x], su[i_w], rows, "y")
         _sampled_rows_check(out["dx"], dyq, 1, 0, wq, 0, 1, su[i_dy], su[i_w], rows, "dx")
-        rows_k = np.sort(rng.choice(4096, 64, replace=False))
+        rows_k = band_rows(4096)
         _sampled_rows_check(out["dw"], xq, 0, 1, dyq, 1, 0, su[i_x], su[i_dy], rows_k, "dw")
         yb = bf16_bits(out["y"])
         assert f32_bits(lin.amax_y.item()) == f32_bits(ogemm.output_amax(yb))
@@ -179,9 +180,12 @@ def test_decoder_projection_health_counts():
 def test_checkpoint_resume_is_bit_identical(tmp_path):
     """Save the scaling state after step 7 of the k_proj trajectory (the 50x batch
     of step 6 is in every window), restore it into a fresh Linear and continue:
-    steps 8 and 9 reproduce the uninterrupted run bit for bit.  Restoring only
-    the scale (dropping the history) does not: the outlier leaves the window
-    early and the next scale changes, the pages' scale-mismatch incident."""
+    steps 8 and 9 reproduce the uninterrupted run bit for bit.  The same saved
+    file also restores the oracle's ScalingState of X, W and dY, and the resumed
+    GPU steps match the oracle's steps from it (every byte, scale, history and
+    cursor exact; GEMMs within tolerance).  Restoring only the scale (dropping
+    the history) does not reproduce the run: the outlier leaves the window early
+    and the next scale changes, the pages' scale-mismatch incident."""
     M = 256
 
     def inputs(step):
@@ -205,10 +209,27 @@ def test_checkpoint_resume_is_bit_identical(tmp_path):
     resumed.load(path)
     scale_only = DelayedScalingLinear(hist_len=16)
     scale_only.scale.copy_(run.scale)
+    # the oracle's scaling state, restored from the same file
+    saved = torch.load(path, map_location="cpu", weights_only=True)
+    states = oracle_states(16)
+    for i, nm in enumerate(("x", "w", "dy")):
+        st = states[nm]
+        st.history = saved["history"][i].numpy().astype(np.float32).copy()
+        st.cursor = int(saved["cursor"][i])
+        st.scale = np.float32(saved["scale"][i].item())
     for step in (8, 9):
         o = resumed.step(*inputs(step))
         scale_only.step(*inputs(step))
         torch.cuda.synchronize()
+        xb, wb, dyb = workloads.llama_tensors("k_proj", step, m=M)
+        oref = olinear.train_step(obf16.widen(xb), obf16.widen(wb), obf16.widen(dyb), states,
+                                  dsg.ALGO_MAX, 0)
+        for key, ck in (("xq", "cast_x"), ("wq", "cast_w"), ("dyq", "cast_dy")):
+            assert np.array_equal(o[key].cpu().numpy(), oref[ck].codes), (step, key)
+        compare_gemm(o["y"], oref["y"], f"resumed y {step}")
+        compare_gemm(o["dx"], oref["dx"], f"resumed dx {step}")
+        compare_gemm(o["dw"], oref["dw"], f"resumed dw {step}")
+        compare_state(resumed, states)
         ro, rs = outs[step]
         for k in ("xq", "wq", "wqt", "dyq"):
             assert torch.equal(o[k], ro[k]), (step, k)

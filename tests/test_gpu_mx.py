@@ -13,8 +13,10 @@ import delayed_scaling_gemm_amd as dsg  # noqa: E402
 import workloads  # noqa: E402
 from oracle import bf16 as obf16  # noqa: E402
 from oracle import mx as omx  # noqa: E402
-from tests.parity import bf16_bits, check_acc, check_bf16_out  # noqa: E402
-from tests.test_gpu_gemm import FP8_PATH_REL, finite_codes, int_codes  # noqa: E402
+from oracle import fp8 as ofp8  # noqa: E402
+from tests.parity import (bf16_bits, check_acc, check_acc_bound, check_bf16_out,  # noqa: E402
+                          fp8_path_bound)
+from tests.test_gpu_gemm import finite_codes, int_codes  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -241,7 +243,8 @@ def test_mx_training_step():
 
 # ---------------------------------------------------------------- FP8 datapath (opt-in)
 # gfx950's block-scaled FP8 MFMA: exact where no product falls out of its
-# summation window, otherwise within the FP8 datapath's measured bound.
+# summation window, otherwise within the FP8 datapath's derived bound
+# (tests.parity.fp8_path_bound on the block-scaled decoded operands).
 
 @pytest.mark.parametrize("fa,fb", FMT_PAIRS)
 @pytest.mark.parametrize("M,N", [(256, 256), (100, 200)])
@@ -269,7 +272,12 @@ def test_mx_fp8_path_within_bound(fa, fb, M, N, K):
     sb = rng.integers(112, 143, (N, K // 32)).astype(np.uint8)
     acc, sum_abs = omx.mx_gemm_nt(a, sa, fa, b, sb, fb)
     c32, _ = _gemm(a, sa, fa, b, sb, fb, out=torch.float32, mma=dsg.MMA_FP8)
-    check_acc(c32.cpu().numpy(), acc, sum_abs, "mx fp8 path", FP8_PATH_REL)
+
+    def scaled(codes, scales, fmt):  # decoded elements times their block scales
+        return ofp8.decode(codes, fmt) * np.ldexp(1.0, np.repeat(scales.astype(np.int64) - 127,
+                                                                  32, axis=1))
+    bound = fp8_path_bound(scaled(a, sa, fa), scaled(b, sb, fb).T, sum_abs)
+    check_acc_bound(c32.cpu().numpy(), acc, bound, "mx fp8 path")
 
 
 def test_mx_linear_matches_the_raw_calls():

@@ -87,32 +87,85 @@ def test_current_cast_is_one_row_of_rowwise():
     assert s == rs[0] and a == ra[0] and sat == 0
 
 
+def _exact_bf16(y: Fraction) -> np.uint16:
+    """Round an exact rational to BF16 (nearest, ties to even) by its own
+    arithmetic: the two BF16 neighbours of y are found from y's binade."""
+    if y == 0:
+        return np.uint16(0)
+    sign = 0x8000 if y < 0 else 0
+    a = abs(y)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 7)               # 8 significant bits
+    lo = (a // ulp) * ulp
+    rem = a - lo
+    up = rem > ulp / 2 or (rem == ulp / 2 and (lo / ulp) % 2 == 1)
+    v = float(lo + ulp if up else lo)
+    bits = int(np.array([v], np.float32).view(np.uint32)[0] >> 16)
+    return np.uint16(bits | sign)
+
+
 def test_scaled_gemm_brute_force():
+    """Exact rational evaluation of the pages' dequant (divide the product sum by
+    the product of the two scales) at scales that are not powers of two."""
     rng = np.random.default_rng(9)
     M, K, N = 3, 5, 4
     a_codes = rng.integers(0, 256, (M, K), dtype=np.uint8)
     b_codes = rng.integers(0, 256, (N, K), dtype=np.uint8)  # stored [N, K], used as op T
     a_codes[(a_codes & 0x7F) == 0x7F] = 0x10                   # no NaN codes
     b_codes[(b_codes & 0x7F) >= 0x7C] = 0x22                   # no E5M2 inf / NaN codes
-    ia = np.array([1.0, 0.25, 3.0], np.float32)
-    ib = np.array([0.5, 2.0, 1.0 / 3.0, 7.0], np.float32)
+    sa = np.array([1.0, 4.48, 3.0], np.float32)
+    sb = np.array([0.5, 57.344, 1.0 / 3.0, 7.0], np.float32)
     acc, _ = ogemm.gemm_exact(a_codes, ofp8.E4M3, ogemm.OP_N, b_codes, ofp8.E5M2, ogemm.OP_T)
-    got = ofin.dequant_vec_to_bf16(acc, ia, ib)
+    got = ofin.dequant_vec_to_bf16(acc, sa, sb)
     da = ofp8.decode(a_codes, ofp8.E4M3)
     db = ofp8.decode(b_codes, ofp8.E5M2)
     for i in range(M):
         for j in range(N):
             exact = sum(Fraction(float(da[i, k])) * Fraction(float(db[j, k])) for k in range(K))
-            y = exact * Fraction(float(ia[i])) * Fraction(float(ib[j]))
-            assert got[i, j] == obf16.round_to_bf16_vec(np.array([float(y)]))[0], (i, j)
+            prod = Fraction(float(np.float32(sa[i] * sb[j])))  # one fp32 multiply
+            assert got[i, j] == _exact_bf16(exact / prod), (i, j)
 
 
-def test_scaled_gemm_reduces_to_per_tensor_for_power_of_two_scales():
+def test_dequant_is_a_division_not_reciprocal_products():
+    """A pin that tells the pages' reading (divide by the scale product) from a
+    kernel-style one (multiply by fl32(1/s_a) and fl32(1/s_b)).  Sums are placed
+    2^-30 (relative) above or below a BF16 rounding midpoint of the quotient, at
+    non-power-of-two scales: the oracle must equal the exact rational quotient
+    rounded to BF16 on every case, while the reciprocal reading (relative error
+    up to a few 2^-24) lands on the other side of the midpoint on some."""
+    rng = np.random.default_rng(12)
+    n = 400
+    sa = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(-6, 7, n)).astype(np.float32)
+    sb = (rng.uniform(1, 2, n) * 3.0).astype(np.float32)
+    hi = rng.integers(0x3F80, 0x4700, n).astype(np.uint32)       # BF16 values in [1, 2^15)
+    lo_v = (hi << 16).view(np.float32).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(lo_v)[1] - 8)                  # BF16 spacing at lo_v
+    mid = lo_v + ulp / 2                                        # midpoint to the next value
+    side = np.where(rng.integers(0, 2, n) == 1, 1.0, -1.0)
+    prod = (sa * sb).astype(np.float32).astype(np.float64)
+    acc = mid * (1.0 + side * 2.0**-30) * prod
+    got = np.array([ofin.dequant_vec_to_bf16(acc[i:i + 1, None], sa[i:i + 1], sb[i:i + 1])[0, 0]
+                    for i in range(n)], np.uint16)
+    exact = np.array([_exact_bf16(Fraction(float(acc[i])) / Fraction(float(prod[i])))
+                      for i in range(n)], np.uint16)
+    np.testing.assert_array_equal(got, exact)
+    recip = obf16.round_to_bf16_vec(
+        acc * np.array([np.float64(ofin.inv_scale(s)) for s in sa]) *
+        np.array([np.float64(ofin.inv_scale(s)) for s in sb]))
+    assert (recip != exact).sum() >= n // 20
+
+
+def test_scaled_gemm_reduces_to_per_tensor_for_equal_scales():
+    """Equal scales along rows and columns give the per-tensor dequant exactly."""
     rng = np.random.default_rng(11)
     a_codes = rng.integers(0, 0x7E, (8, 16), dtype=np.uint8)
     b_codes = rng.integers(0, 0x7E, (16, 6), dtype=np.uint8)
     acc, _ = ogemm.gemm_exact(a_codes, ofp8.E4M3, ogemm.OP_N, b_codes, ofp8.E4M3, ogemm.OP_N)
-    sa, sb = np.float32(64.0), np.float32(0.5)
-    per_tensor = ogemm.dequant_to_bf16(acc, sa, sb)
-    vec = ofin.dequant_vec_to_bf16(acc, np.full(8, 1 / sa, np.float32), np.full(6, 1 / sb, np.float32))
-    np.testing.assert_array_equal(per_tensor, vec)
+    for sa, sb in ((np.float32(64.0), np.float32(0.5)), (np.float32(4.48), np.float32(57.344))):
+        per_tensor = ogemm.dequant_to_bf16(acc, sa, sb)
+        vec = ofin.dequant_vec_to_bf16(acc, np.full(8, sa, np.float32), np.full(6, sb, np.float32))
+        np.testing.assert_array_equal(per_tensor, vec)
