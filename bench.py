@@ -16,8 +16,10 @@ set.  Per-kernel times (the roofline figures) come from HIP events on the
 stream the library launches on around K back-to-back launches of each call of
 the step (inputs rotated over the sets), run just before the timed region.
 
-The line also carries context figures that are not `value`: the same GEMMs on
-the FP8 matrix instructions (`fp8_mma_path_tflops`), the 2^30-element stress
+The forward GEMM runs on gfx950's FP8 matrix instructions, the dX and dW GEMMs
+on the exact F16-widened datapath (DelayedScalingLinear's defaults).  The line
+also carries context figures that are not `value`: each GEMM on the other
+datapath (`other_datapath_tflops`), the 2^30-element stress
 casts (`cast_stress`), per-token / per-channel / current scaling of the same
 Linear's forward (`finer_scaling`), the fused AdamW step on the 4096 x 4096
 weight that also writes the next forward's FP8 weights (`optimizer`, against
@@ -52,6 +54,8 @@ PEAK_F16_TFLOPS = 2500.0   # MI355X dense F16 MFMA (the instruction of the exact
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 N_SETS = 4
 CPU_SAMPLE_ROWS = 8192
+CPU_CAST_SAMPLE = 1 << 24   # elements of the 2^30 stress tensor cast by the oracle
+CPU_GEMM_ROWS = 512         # rows of the forward 4096 Linear's GEMM computed by the oracle
 KERNEL_SOURCES = ["delayed_scaling_gemm_amd/csrc/gemm_kernel.h",
                   "delayed_scaling_gemm_amd/csrc/device_common.h"]
 TRAFFIC_FILE = "profiles/gemm_linear_4096_m16384_traffic.txt"
@@ -147,6 +151,44 @@ def cpu_baseline(xb, wb, dyb, rows=CPU_SAMPLE_ROWS):
     }
 
 
+def cpu_other(workloads, cast_sample):
+    """The oracle on bounded samples of two more workloads (CPU, one thread for
+    the numpy casts, BLAS threads for the fp64 GEMM): the amax + E4M3 cast of the
+    first 2^24 elements of the 2^30-element stress tensor (3 algorithmic bytes
+    per element), and the exact GEMM of the first 512 token rows of the forward
+    4096 Linear (8192 x 4096 x 4096, E4M3 both; the rows cast by the oracle)."""
+    from oracle import amax as oamax
+    from oracle import bf16 as obf16
+    from oracle import fp8 as ofp8
+    from oracle import gemm as ogemm
+
+    out = {}
+    if cast_sample is not None:
+        x = obf16.widen(cast_sample)
+        t0 = time.perf_counter()
+        oamax.amax(x)
+        ofp8.cast(x, np.float32(1.0), ofp8.E4M3)
+        dt = time.perf_counter() - t0
+        out["amax_cast_2e30_stress"] = {
+            "sample": f"first {cast_sample.size} elements, amax + cast to E4M3 at scale 1",
+            "seconds": round(dt, 3), "GB/s": round(3.0 * cast_sample.size / dt / 1e9, 3)}
+    xb, wb = workloads.forward_4096()
+    x = obf16.widen(xb[:CPU_GEMM_ROWS])
+    w = obf16.widen(wb)
+    xs, ws = np.float32(448.0) / oamax.amax(x), np.float32(448.0) / oamax.amax(w)
+    cx, _ = ofp8.cast(x, xs, ofp8.E4M3)
+    cw, _ = ofp8.cast(w, ws, ofp8.E4M3)
+    t0 = time.perf_counter()
+    acc, _ = ogemm.gemm_exact(cx, ofp8.E4M3, ogemm.OP_N, cw, ofp8.E4M3, ogemm.OP_N)
+    ogemm.dequant_to_bf16(acc, xs, ws)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * CPU_GEMM_ROWS * w.shape[0] * w.shape[1]
+    out["gemm_forward_4096"] = {
+        "sample": f"{CPU_GEMM_ROWS} of 8192 rows, exact fp64 GEMM (with sum|ab|) and BF16 dequant",
+        "seconds": round(dt, 3), "TFLOP/s": round(flop / dt / 1e12, 6)}
+    return out
+
+
 def copy_calibration(torch, mib: int):
     n = mib << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -176,6 +218,7 @@ def stress_cast(torch, dsg, workloads, dev, iters=10):
     print("[bench] stress cast 2^30", file=sys.stderr, flush=True)
     bits = workloads.big_cast_input(n)
     x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    sample = bits[:CPU_CAST_SAMPLE].copy()  # for the oracle's timing on the CPU
     del bits
     q = torch.empty(n, dtype=torch.uint8, device=dev)
     s = torch.ones(1, dtype=torch.float32, device=dev)
@@ -203,7 +246,7 @@ def stress_cast(torch, dsg, workloads, dev, iters=10):
                    "frac_hbm": round(2.0 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     del x, q
     torch.cuda.empty_cache()
-    return out
+    return out, sample
 
 
 def optimizer_report(torch, dsg, workloads, dev, rows=4096, cols=4096, iters=10):
@@ -391,7 +434,7 @@ def configs_report(torch, dsg, workloads, dev, iters=5):
     b, su = lin._bufs, lin.scale_used
     g_ms = time_launches(torch, stream, lambda: fp8ds_gemm(
         OP_N, OP_T, M, N, K, b["xq"], E4M3, K, su[0:1], b["wqt"], E4M3, K, su[1:2], b["y"], N,
-        lin.amax_y), iters)
+        lin.amax_y, mma=lin.fwd_datapath(K)), iters)
     out["forward_4096_m8192"] = {"step_ms": round(step_ms, 4), "gemm_ms": round(g_ms, 4),
                                  "gemm_tflops": tf(2 * M * N * K, g_ms),
                                  "gemm_frac_fp8_peak": round(tf(2 * M * N * K, g_ms) /
@@ -410,7 +453,8 @@ def configs_report(torch, dsg, workloads, dev, iters=5):
         b, su = lin._bufs, lin.scale_used
         calls = {
             "fwd_nt": lambda: fp8ds_gemm(OP_N, OP_T, M, N, K, b["xq"], E4M3, K, su[0:1], b["wqt"],
-                                         E4M3, K, su[1:2], b["y"], N, lin.amax_y),
+                                         E4M3, K, su[1:2], b["y"], N, lin.amax_y,
+                                         mma=lin.fwd_datapath(K)),
             "dgrad_nt": lambda: fp8ds_gemm(OP_N, OP_T, M, K, N, b["dyq"], E5M2, N, su[2:3],
                                            b["wq"], E4M3, N, su[1:2], b["dx"], K),
             "wgrad_tn": lambda: fp8ds_gemm(OP_T, OP_N, K, N, M, b["xq"], E4M3, K, su[0:1],
@@ -491,12 +535,12 @@ def main():
             lambda: fp8ds_cast(x, E4M3, s[0:1], xq, None, su[0:1], am[0:1], sat[0:1]),
             lambda: fp8ds_cast(w, E4M3, s[1:2], wq, wqt, su[1:2], am[1:2], sat[1:2]),
             lambda: fp8ds_gemm(OP_N, OP_T, M, N, K, xq, E4M3, K, su[0:1], wqt, E4M3, K, su[1:2], y,
-                               N, lin.amax_y),
+                               N, lin.amax_y, mma=lin.fwd_datapath(K)),
             lambda: fp8ds_cast(dy, E5M2, s[2:3], dyq, None, su[2:3], am[2:3], sat[2:3]),
             lambda: fp8ds_gemm(OP_N, OP_T, M, K, N, dyq, E5M2, N, su[2:3], wq, E4M3, N, su[1:2],
-                               dx, K),
+                               dx, K, mma=lin.mma_bwd),
             lambda: fp8ds_gemm(OP_T, OP_N, K, N, M, xq, E4M3, K, su[0:1], dyq, E5M2, N, su[2:3],
-                               dw, N),
+                               dw, N, lin.amax_dw, mma=lin.mma_bwd),
             lambda: fp8ds_scale_update(lin.history, lin.cursor, am, lin.fmts, lin.algo, lin.margin,
                                        s),
         ]
@@ -549,6 +593,23 @@ def main():
     wall = time.perf_counter() - t_wall0
     ms_per_step = e_start.elapsed_time(e_end) / args.steps
 
+    # Step-time distribution: a separate pass of at least 50 steps with an event
+    # at every step boundary (each event adds a few microseconds to its step, so
+    # `value` comes from the region above, timed at its ends only).
+    n_dist = max(50, args.steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n_dist):
+        x, w, dy = sets[i % N_SETS]
+        step(x, w, dy)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    dist = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n_dist)])
+    step_dist = {"steps": n_dist, "median_ms": round(float(np.median(dist)), 4),
+                 "p10_ms": round(float(np.percentile(dist, 10)), 4),
+                 "p90_ms": round(float(np.percentile(dist, 90)), 4)}
+
     flop_gemm = 2.0 * M * K * N
     value = 3 * flop_gemm / (ms_per_step * 1e-3) / 1e12
     avg = {n: float(per[n]) for n in names}
@@ -577,7 +638,8 @@ def main():
         "config": {
             "workload": "fwd+bwd FP8 delayed-scaling Linear, 4096 hidden, M=16384 tokens "
                         "(X, W, dY bf16; HYBRID E4M3/E5M2; history 16, max, margin 0; "
-                        "exact F16-widened GEMM datapath)",
+                        "forward GEMM on FP8 MFMA, dX and dW GEMMs on the exact "
+                        "F16-widened datapath)",
             "M": M, "K": K, "N": N, "hist_len": HIST_LEN,
         },
         "roofline": {
@@ -603,38 +665,46 @@ def main():
         "gemm_tflops": gemm_tflops,
         "cast_gbps": cast_gbps,
         "kernel_ms": {n: round(v, 4) for n, v in avg.items()},
+        "step_ms_distribution": step_dist,
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "sum_of_kernel_ms": round(sum(avg.values()), 4),
     }
 
     if not args.no_fp8_path:
-        # context only: the same three GEMMs on the FP8 matrix instructions, whose
-        # summation drops small products (not the product path, see fp8ds_mma)
+        # context only: each GEMM of the step on the other datapath -- the forward
+        # on the exact F16-widened path, the backward products on the FP8 matrix
+        # instructions (whose summation misses the tolerance on heavy-tailed
+        # gradients, see fp8ds_mma)
         b = lin._bufs
         su = lin.scale_used
+        other = {0: 1, 1: 0}
         calls = {
             "gemm_fwd_nt": lambda: fp8ds_gemm(OP_N, OP_T, M, N, K, b["xq"], E4M3, K, su[0:1],
                                               b["wqt"], E4M3, K, su[1:2], b["y"], N, None,
-                                              mma=MMA_FP8),
+                                              mma=other[lin.fwd_datapath(K)]),
             "gemm_dgrad_nt": lambda: fp8ds_gemm(OP_N, OP_T, M, K, N, b["dyq"], E5M2, N, su[2:3],
                                                 b["wq"], E4M3, N, su[1:2], b["dx"], K, None,
-                                                mma=MMA_FP8),
+                                                mma=other[lin.mma_bwd]),
             "gemm_wgrad_tn": lambda: fp8ds_gemm(OP_T, OP_N, K, N, M, b["xq"], E4M3, K, su[0:1],
                                                 b["dyq"], E5M2, N, su[2:3], b["dw"], N, None,
-                                                mma=MMA_FP8),
+                                                mma=other[lin.mma_bwd]),
         }
-        fp8 = {}
+        alt = {}
         for n, fn in calls.items():
             fn()
             ms = time_launches(torch, stream, fn, 10)
-            fp8[n] = round(flop_gemm / (ms * 1e-3) / 1e12, 1)
-        result["fp8_mma_path_tflops"] = fp8
+            alt[n] = round(flop_gemm / (ms * 1e-3) / 1e12, 1)
+        result["other_datapath_tflops"] = {
+            "datapaths": {"gemm_fwd_nt": "exact" if lin.fwd_datapath(K) == MMA_FP8 else "fp8",
+                          "gemm_dgrad_nt": "exact" if lin.mma_bwd == MMA_FP8 else "fp8",
+                          "gemm_wgrad_tn": "exact" if lin.mma_bwd == MMA_FP8 else "fp8"},
+            **alt}
 
     if not args.no_finer:
         x0, w0, dy0 = sets[0]
         result["finer_scaling"] = finer_report(torch, dsg, x0, w0, dy0)
     if not args.no_stress:
-        result["cast_stress"] = stress_cast(torch, dsg, workloads, dev)
+        result["cast_stress"], cast_sample = stress_cast(torch, dsg, workloads, dev)
         # the metric's amax+cast figure: the 2^30-element bandwidth workload
         st = result["cast_stress"]["e4m3"]
         result["cast_roofline"] = {
@@ -650,6 +720,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(xb, wb, dyb)
+        result["cpu_baseline"]["other_workloads"] = cpu_other(
+            workloads, cast_sample if not args.no_stress else None)
     print(json.dumps(result), flush=True)
 
 

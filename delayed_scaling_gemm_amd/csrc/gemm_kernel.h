@@ -443,9 +443,11 @@ __device__ __forceinline__ float dq(float a, float r, float c) {
   if constexpr (VS) return (a * r) * c;
   else return a * r;
 }
-// `stage0`, `stage1`: the two halves of the operand tiles' LDS (at least 2 WTM WTN
-// 2 bytes each), free once every wave has passed the epilogue's first barrier.
-template <int BM, int BN, int FM, int FN, int WTM, int WTN, bool VS = false>
+// `stage0`, `stage1`: the two halves of the operand tiles' LDS (at least NW/2 WTM
+// WTN 2 bytes each), free once every wave has passed the epilogue's first
+// barrier; the first NW/2 waves stage their blocks in `stage0`, the others in
+// `stage1`.  `red` holds NW words.
+template <int BM, int BN, int FM, int FN, int WTM, int WTN, bool VS = false, int NW = 4>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM][FN], int64_t m0,
                                          int64_t n0, int wm, int wn, int tid, int64_t bz, float d,
                                          uint32_t* red, uint8_t* stage0, uint8_t* stage1) {
@@ -466,9 +468,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
       constexpr int RB = WTN * 2;   // bytes per staged row
       constexpr int CH = RB / 16;   // 16-byte chunks per row
       constexpr int RPI = 64 / CH;  // rows per read-back instruction
-      static_assert(2 * WTM * RB <= BM * 2 * kRowBytes && 2 * WTM * RB <= BN * 2 * kRowBytes,
-                    "two waves' blocks fit in each half of the operand tiles' LDS");
-      uint8_t* st = (wave < 2 ? stage0 : stage1) + (wave & 1) * WTM * RB;
+      static_assert((NW / 2) * WTM * RB <= BM * 2 * kRowBytes &&
+                        (NW / 2) * WTM * RB <= BN * 2 * kRowBytes,
+                    "half of the waves' blocks fit in each half of the operand tiles' LDS");
+      uint8_t* st = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * WTM * RB;
       __syncthreads();  // every wave has finished reading the operand tiles
       u16x2_t am2 = {0, 0};
 #pragma unroll
@@ -577,7 +580,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
     if (lane == 0) red[wave] = amax;
     __syncthreads();
     if (tid == 0) {
-      const uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
+      uint32_t m = red[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) m = max(m, red[w]);
       atomicMax(p.amax_c + bz, canonical_amax_bits(m));
     }
   }

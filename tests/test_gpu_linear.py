@@ -107,8 +107,9 @@ def _sampled_rows_check(gpu_out, a_codes, fa, opa, b_codes, fb, opb, sa, sb, row
 def test_fwd_bwd_4096_full_size_sampled():
     """The M=16384, 4096-hidden Linear at full size, launched exactly as the
     benchmark launches it: all cast bytes on a sample, amax and saturation exact,
-    rows of each GEMM output against the oracle (first, last and one moving row of
-    every 256-row tile band), output amax exact."""
+    every output of the forward GEMM (FP8 matrix instructions) and rows of the
+    backward GEMMs (first, last and one moving row of every 256-row tile band)
+    against the oracle, output amax exact."""
     xb, wb, dyb = workloads.fwd_bwd_4096()
     print("[fwd_bwd_4096] inputs ready", flush=True)
     lin = DelayedScalingLinear(hist_len=16)
@@ -128,8 +129,11 @@ def test_fwd_bwd_4096_full_size_sampled():
         i_x, i_w, i_dy = 0, 1, 2
         su = lin.scale_used.cpu().numpy()
         assert f32_bits(su[i_x]) == f32_bits(states["x"].scale)
+        # the forward runs on the FP8 matrix instructions: every output row checked
+        for r0 in range(0, 16384, 2048):
+            _sampled_rows_check(out["y"], xq, 0, 0, wq, 0, 0, su[i_x], su[i_w],
+                                np.arange(r0, r0 + 2048), "y")
         rows = band_rows(16384)
-        _sampled_rows_check(out["y"], xq, 0, 0, wq, 0, 0, su[i_x], su[i_w], rows, "y")
         _sampled_rows_check(out["dx"], dyq, 1, 0, wq, 0, 1, su[i_dy], su[i_w], rows, "dx")
         rows_k = band_rows(4096)
         _sampled_rows_check(out["dw"], xq, 0, 1, dyq, 1, 0, su[i_x], su[i_dy], rows_k, "dw")
