@@ -280,12 +280,12 @@ struct LoaderSel<false, ROWS, NT, KB> {
 };
 
 // KC source loaded straight into LDS (gfx950 global_load_lds_dwordx4: each
-// lane's 16 bytes land at LDS base + 16 * lane, no registers involved).  A
-// wave instruction fills one 1 KiB segment = 8 LDS rows of 128 bytes; lane l
-// takes physical chunk l % 8 of row l / 8 and therefore loads the logical chunk
-// (l % 8) ^ swz(row), which keeps the swizzled layout of lds_off.  Requires the
-// stage to lie inside K (K a multiple of 128); rows past the matrix are clamped
-// to its last row (they only feed outputs that are never stored).
+// lane's 16 bytes land at LDS base + 16 * lane, no registers involved; issued
+// as buffer loads, see LoaderKCDirect).  A wave instruction fills one 1 KiB
+// segment = 8 LDS rows of 128 bytes; lane l takes physical chunk l % 8 of row
+// l / 8 and therefore loads the logical chunk (l % 8) ^ swz(row), which keeps
+// the swizzled layout of lds_off.  Requires the stage to lie inside K (K a
+// multiple of 128).
 // Wait until every vector-memory operation of this wave has completed.  Direct
 // LDS loads write no registers, so the compiler does not wait for them on its
 // own, and a workgroup barrier's fence only waits for LDS operations.
@@ -299,29 +299,56 @@ __device__ __forceinline__ void vmem_wait_n() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Buffer resource of the bytes [base, base + nbytes): a load at an offset past
+// nbytes returns zeros (dword 3 = 0x00020000: 32-bit data format, the gfx9
+// setting for raw byte-addressed buffers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const uint8_t* base, int64_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)nbytes, 0x00020000);
+}
+
+// The loads go through a buffer resource whose base is the tile's first row, so
+// a load's address is a per-lane offset (row within the 8-row segment and
+// swizzled chunk, fixed for the kernel) plus a scalar offset (segment row and
+// stage K): no per-load address arithmetic beyond one XOR and one add, and rows
+// past the matrix read as zeros (they only feed outputs that are never stored).
+// Requires every offset of the operand below 2^31 (checked by the caller).
 template <int ROWS, int NT>
 struct LoaderKCDirect {
   static constexpr int kSegs = ROWS / 8;
   static constexpr int kWaves = NT / 64;
   static constexpr int kPerWave = kSegs / kWaves;
   static_assert(kPerWave * kWaves == kSegs, "segments must divide among the waves");
+  __amdgpu_buffer_rsrc_t rsrc;
+  int ld;
+  int w;         // wave index (scalar)
+  int lane_row;  // (lane / 8) * ld
+  int colx;      // ((lane % 8) ^ (lane / 8)) * 16
 
-  __device__ __forceinline__ static void issue(const uint8_t* __restrict__ src, int64_t ld,
-                                               int64_t row0, int64_t rows, int64_t k0,
-                                               uint8_t* lds, int tid) {
-    const int lane = tid & 63, w = tid >> 6;
-    const int rr = lane >> 3, pc = lane & 7;
+  // rows [row0, rows) of a [rows x K] byte matrix with leading dimension ld
+  __device__ __forceinline__ LoaderKCDirect(const uint8_t* src, int64_t ld_, int64_t row0,
+                                            int64_t rows, int64_t K, int tid) {
+    ld = (int)ld_;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, rr = lane >> 3, pc = lane & 7;
+    lane_row = rr * ld;
+    colx = (pc ^ rr) << 4;
+    rsrc = byte_rsrc(src + row0 * ld_, (rows - row0 - 1) * ld_ + K);
+  }
+
+  // issues this wave's load instructions i in [lo, hi) of the stage at k0.
+  // Instruction i fills LDS segment seg = w kPerWave + i (rows 8 seg .. +8);
+  // lane l takes physical chunk l % 8 of row r = 8 seg + l / 8, i.e. the
+  // logical chunk (l % 8) ^ swz(r) = (l % 8) ^ (l / 8) ^ ((seg / 2) % 8).
+  __device__ __forceinline__ void issue(int64_t k0, uint8_t* lds, int lo = 0,
+                                        int hi = kPerWave) const {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
+      if (i < lo || i >= hi) continue;
       const int seg = w * kPerWave + i;
-      const int r = seg * 8 + rr;
-      const int c = pc ^ swz(r);
-      int64_t gr = row0 + r;
-      gr = gr < rows ? gr : rows - 1;
-      const uint8_t* g = src + gr * ld + k0 + c * 16;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                       (void __attribute__((address_space(3)))*)(lds + seg * 1024),
-                                       16, 0, 0);
+      const int voff = lane_row + (colx ^ (((seg >> 1) & 7) << 4));
+      const int soff = seg * 8 * ld + (int)k0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (void __attribute__((address_space(3)))*)(lds + seg * 1024), 16, voff, soff, 0, 0);
     }
   }
 };
@@ -333,8 +360,9 @@ struct LoaderKCDirect {
 // 16 distinct chunk columns).  A wave instruction fills 1 KiB = 1024 / ROWS
 // rows; lane l takes physical chunk l % (ROWS / 16) of its row and loads the
 // logical chunk that lands there.  Requires whole 16-byte chunks (rows a
-// multiple of 16; chunks past the matrix are clamped to its last chunk, feeding
-// only outputs that are never stored) and the stage inside K.
+// multiple of 16) and the stage inside K.  Chunks past the matrix's last
+// column read the next k row, or zeros past the end of the matrix; either
+// feeds only outputs that are never stored.
 template <int ROWS>
 __device__ __forceinline__ int mn_swz(int k) {
   return ROWS >= 256 ? (k & 7) << 1 : (k & 7);
@@ -351,26 +379,54 @@ struct LoaderMNDirect {
   static constexpr int kSegs = 128 / kRps;    // wave instructions per stage (128 k rows)
   static constexpr int kWaves = NT / 64;
   static constexpr int kPerWave = kSegs / kWaves;
-  static_assert(kCpr >= 8 && kPerWave * kWaves == kSegs, "tile shape not supported");
+  static_assert((ROWS == 128 || ROWS == 256) && kPerWave * kWaves == kSegs,
+                "tile shape not supported");
+  __amdgpu_buffer_rsrc_t rsrc;
+  int ld;
+  int w;         // wave index (scalar)
+  int lane_row;  // (lane / kCpr) * ld
+  int colx;      // swizzled chunk offset of even segments
+  int seg_flip;  // XOR of the chunk offset for odd segments (256-row tiles)
 
-  __device__ __forceinline__ static void issue(const uint8_t* __restrict__ src, int64_t ld,
-                                               int64_t row0, int64_t rows, int64_t k0,
-                                               uint8_t* lds, int tid) {
-    const int lane = tid & 63, w = tid >> 6;
-    const int rr = lane / kCpr, pc = lane % kCpr;
+  // columns [row0, rows) of a [K x rows] byte matrix with leading dimension ld
+  __device__ __forceinline__ LoaderMNDirect(const uint8_t* src, int64_t ld_, int64_t row0,
+                                            int64_t rows, int64_t K, int tid) {
+    ld = (int)ld_;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, rr = lane / kCpr, pc = lane % kCpr;
+    // k = kRps seg + rr: for 128-row tiles k % 8 = rr, for 256-row tiles
+    // k % 8 = 4 (seg % 2) + rr, so the swizzled chunk is fixed per lane up to a
+    // flip of bit 3 on odd segments
+    const int c = ROWS >= 256 ? pc ^ (rr << 1) : pc ^ rr;
+    lane_row = rr * ld;
+    colx = c << 4;
+    seg_flip = ROWS >= 256 ? (8 << 4) : 0;
+    rsrc = byte_rsrc(src + row0, (K - 1) * ld_ + (rows - row0));
+  }
+
+  __device__ __forceinline__ void issue(int64_t k0, uint8_t* lds, int lo = 0,
+                                        int hi = kPerWave) const {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
+      if (i < lo || i >= hi) continue;
       const int seg = w * kPerWave + i;
-      const int k = seg * kRps + rr;
-      const int c = pc ^ mn_swz<ROWS>(k);
-      int64_t gm = row0 + c * 16;
-      gm = gm + 16 <= rows ? gm : rows - 16;
-      const uint8_t* g = src + (k0 + k) * ld + gm;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                       (void __attribute__((address_space(3)))*)(lds + seg * 1024),
-                                       16, 0, 0);
+      const int voff = lane_row + (colx ^ ((seg & 1) ? seg_flip : 0));
+      const int soff = ((int)k0 + seg * kRps) * ld;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (void __attribute__((address_space(3)))*)(lds + seg * 1024), 16, voff, soff, 0, 0);
     }
   }
+};
+
+template <bool KC, int ROWS, int NT>
+struct DirectSel;
+template <int ROWS, int NT>
+struct DirectSel<true, ROWS, NT> {
+  using type = LoaderKCDirect<ROWS, NT>;
+};
+template <int ROWS, int NT>
+struct DirectSel<false, ROWS, NT> {
+  using type = LoaderMNDirect<ROWS, NT>;
 };
 
 // Direct-load instructions one wave issues for one operand's stage.
@@ -622,7 +678,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t bz = blockIdx.y;
 
@@ -686,16 +742,21 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   // goes into the buffer of stage k right after stage k's barrier (all waves
   // have read it by then), and that barrier's wait on outstanding loads makes
   // stage k + 1 complete before it is read.
-  auto issue_direct = [&](int kt, int buf) {
+  // The wave's load instructions of a stage, A's then B's, numbered 0 ..
+  // kIssuesA + kIssuesB; issue_direct issues those in [lo, hi).
+  constexpr int kIssuesA = direct_issues<A_KC, BM, NT>();
+  constexpr int kIssuesB = direct_issues<B_KC, BN, NT>();
+  using DLA = typename DirectSel<A_KC, BM, NT>::type;
+  using DLB = typename DirectSel<B_KC, BN, NT>::type;
+  const DLA dla(DIRECT ? A : nullptr, p.lda, m0, M, K, tid);
+  const DLB dlb(DIRECT ? B : nullptr, p.ldb, n0, N, K, tid);
+  auto issue_direct = [&](int kt, int buf, int lo = 0, int hi = 1 << 20) {
     if constexpr (DIRECT) {
-      if constexpr (A_KC)
-        LoaderKCDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
-      else
-        LoaderMNDirect<BM, NT>::issue(A, p.lda, m0, M, (int64_t)kt * KB, lds_a[buf], tid);
-      if constexpr (B_KC)
-        LoaderKCDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
-      else
-        LoaderMNDirect<BN, NT>::issue(B, p.ldb, n0, N, (int64_t)kt * KB, lds_b[buf], tid);
+      const int la = lo, ha = hi < kIssuesA ? hi : kIssuesA;
+      const int lb = lo > kIssuesA ? lo - kIssuesA : 0;
+      const int hb = hi < kIssuesA + kIssuesB ? hi - kIssuesA : kIssuesB;
+      dla.issue((int64_t)kt * KB, lds_a[buf], la, ha);
+      dlb.issue((int64_t)kt * KB, lds_b[buf], lb, hb);
     }
   };
   if constexpr (EXACT) {
@@ -806,8 +867,21 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       widen_step(ra[0], rb[0], 0, ha[0], hb[0], 0, true);
     }
 
-    auto stage = [&](int kt, auto more_tag) {
+    // Direct loads of stage kt + 2 go into stage kt's buffer once stage kt's
+    // barrier (step 6) has passed: half of them in step 6, half in step 7, each
+    // load instruction placed after one of the step's MFMAs.  Issued in one burst
+    // after the barrier, the 16 load instructions of a wave held up its MFMAs
+    // (~20% of the kernel's time, measured by leaving the loads out).  They are
+    // not spread further into the next stage: an LDS read that follows a direct
+    // load in the same iteration makes the compiler wait for the load.
+    constexpr int kIss = kIssuesA + kIssuesB;
+    constexpr int kPart0 = kIss / 2;
+    // LOADS: this stage issues the direct loads of stage kt + 2 (every stage but
+    // the last two; a separate instantiation, so that no branch separates the
+    // loads from the MFMAs they are interleaved with)
+    auto stage = [&](int kt, auto more_tag, auto loads_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
+      constexpr bool LOADS = DIRECT && decltype(loads_tag)::value;
       const int cur = kt & 1;
       if constexpr (MX) take_scales(0);  // units 0, 1 of this stage (loaded a stage ago)
       if constexpr (MORE && !DIRECT) {
@@ -829,9 +903,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
             if constexpr (DIRECT) vmem_wait_all();
             __syncthreads();
             read_unit(cur ^ 1, 0, ra[0], rb[0]);
-            if constexpr (DIRECT) {
-              if (kt + 2 < nk) issue_direct(kt + 2, cur);
-            }
+            if constexpr (LOADS) issue_direct(kt + 2, cur, 0, kPart0);
+          }
+          if constexpr (LOADS) {
+            if (t == 7) issue_direct(kt + 2, cur, kPart0, kIss);
           }
         }
         if constexpr (MX) {
@@ -849,14 +924,26 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
           widen_step(ra[0], rb[0], 0, ha[0], hb[0], 0, true);
         }
         mma(ha[t & 1], hb[t & 1]);
+        if constexpr (LOADS) {
+          if (t >= 6) {  // one direct load after each of the first MFMAs
+#pragma unroll
+            for (int k = 0; k < kIss / 2; ++k) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+            }
+          }
+        }
         // keep each step's reads, stores and widening inside the step they were
         // placed in: the scheduler otherwise pulls the widening next to the LDS
         // reads it depends on and waits for them
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
-    if (nk > 0) stage(nk - 1, std::false_type{});
+    int kt = 0;
+    if constexpr (DIRECT)
+      for (; kt + 2 < nk; ++kt) stage(kt, std::true_type{}, std::true_type{});
+    for (; kt + 1 < nk; ++kt) stage(kt, std::true_type{}, std::false_type{});
+    if (nk > 0) stage(nk - 1, std::false_type{}, std::false_type{});
   } else {
     u32x4 ra[2][FM][2], rb[2][FN][2];  // two chunks per step, by step parity
     // Step s of a stage takes, per lane, 32 consecutive K values of its row:
@@ -1036,8 +1123,14 @@ static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream) {
       return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && ld % 16 == 0 &&
              (q.batch == 1 || stride % 16 == 0);
     };
-    const bool a_ok = aligned(q.A, q.lda, q.stride_a) && (A_KC || q.M % 16 == 0);
-    const bool b_ok = aligned(q.B, q.ldb, q.stride_b) && (B_KC || q.N % 16 == 0);
+    // the buffer loads address each operand with 32-bit offsets
+    auto fits = [&](int64_t rows, int64_t cols, int64_t ld) {
+      return (rows + 256) * ld + cols < (int64_t(1) << 31);  // a tile may run past `rows`
+    };
+    const bool a_ok = aligned(q.A, q.lda, q.stride_a) && (A_KC || q.M % 16 == 0) &&
+                      (A_KC ? fits(q.M, q.K, q.lda) : fits(q.K, q.M, q.lda));
+    const bool b_ok = aligned(q.B, q.ldb, q.stride_b) && (B_KC || q.N % 16 == 0) &&
+                      (B_KC ? fits(q.N, q.K, q.ldb) : fits(q.K, q.N, q.ldb));
     if (q.K % 128 == 0 && a_ok && b_ok)
       return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, true, VS>(q, stream);
   }
