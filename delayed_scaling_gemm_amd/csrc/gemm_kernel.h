@@ -1049,8 +1049,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       __syncthreads();
       read_step(0, 0, ra[0], rb[0]);
     }
-    auto stage = [&](int kt, auto more_tag) {
+    // LOADS: the stage issues the direct loads of stage kt + 2, one after each
+    // of its second step's MFMAs (a separate instantiation for the last two
+    // stages, so that no branch separates the loads from those MFMAs)
+    auto stage = [&](int kt, auto more_tag, auto loads_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
+      constexpr bool LOADS = DIRECT && decltype(loads_tag)::value;
       const int cur = kt & 1;
       if constexpr (MORE && !DIRECT) {
         la.load(A, p.lda, m0, M, (int64_t)(kt + 1) * KB, K, tid);
@@ -1073,14 +1077,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         if constexpr (DIRECT) vmem_wait_all();
         __syncthreads();
         read_step(cur ^ 1, 0, ra[0], rb[0]);
-        if constexpr (DIRECT) {
-          if (kt + 2 < nk) issue_direct(kt + 2, cur);
-        }
+        if constexpr (LOADS) issue_direct(kt + 2, cur);
       }
       mma(ra[1], rb[1], 1);
+      if constexpr (LOADS) {
+#pragma unroll
+        for (int k = 0; k < kIssuesA + kIssuesB; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+      }
     };
-    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
-    if (nk > 0) stage(nk - 1, std::false_type{});
+    int kt = 0;
+    if constexpr (DIRECT)
+      for (; kt + 2 < nk; ++kt) stage(kt, std::true_type{}, std::true_type{});
+    for (; kt + 1 < nk; ++kt) stage(kt, std::true_type{}, std::false_type{});
+    if (nk > 0) stage(nk - 1, std::false_type{}, std::false_type{});
   }
 
   epilogue<BM, BN, FM, FN, WTM, WTN, VS>(p, acc, m0, n0, wm, wn, tid, bz, d, red,
