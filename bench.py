@@ -227,9 +227,12 @@ def stress_cast(torch, dsg, workloads, dev, iters=10):
     stream = torch.cuda.current_stream()
     out = {}
     for fmt, name in ((dsg.E4M3, "e4m3"), (dsg.E5M2, "e5m2")):
+        # timed: the accumulating call (the cast kernel alone; the amax and the
+        # count combine over the repeats); reported counts: one resetting call
+        dsg.fp8ds_cast_acc(x, fmt, s, q, None, None, am, sat)
+        ms = time_launches(torch, stream,
+                           lambda: dsg.fp8ds_cast_acc(x, fmt, s, q, None, None, am, sat), iters)
         dsg.fp8ds_cast(x, fmt, s, q, None, None, am, sat)
-        ms = time_launches(torch, stream, lambda: dsg.fp8ds_cast(x, fmt, s, q, None, None, am, sat),
-                           iters)
         gbps = 3.0 * n / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
                      "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "saturated": int(sat.item())}
@@ -503,8 +506,8 @@ def main():
 
     import delayed_scaling_gemm_amd as dsg
     import workloads
-    from delayed_scaling_gemm_amd import (E4M3, E5M2, MMA_FP8, OP_N, OP_T, fp8ds_cast,
-                                          fp8ds_gemm, fp8ds_scale_update)
+    from delayed_scaling_gemm_amd import (E4M3, E5M2, MMA_FP8, OP_N, OP_T, fp8ds_cast_acc,
+                                          fp8ds_gemm, fp8ds_gemm_acc, fp8ds_scale_update_clear)
     from delayed_scaling_gemm_amd.linear import DelayedScalingLinear
 
     dev = torch.device("cuda:0")
@@ -527,27 +530,31 @@ def main():
              "scale_update"]
 
     def launches(x, w, dy):
-        """The launches of DelayedScalingLinear.step, one closure each, in order."""
+        """The launches of DelayedScalingLinear.step, one closure each, in order
+        (for the per-kernel figures; they combine into one accumulator set)."""
         b = lin._bufs
         xq, wq, wqt, y, dyq, dx, dw = (b[k] for k in ("xq", "wq", "wqt", "y", "dyq", "dx", "dw"))
-        s, su, am, sat = lin.scale, lin.scale_used, lin.amax, lin.sat
+        slot = lin._slot
+        s, su = lin.scale, lin.scale_used
+        am, sat = lin._amax_of(slot), lin._sat_of(slot)
+        amy = lin._acc[slot, 3:4].view(torch.float32)
+        amdw = lin._acc[slot, 4:5].view(torch.float32)
         return [
-            lambda: fp8ds_cast(x, E4M3, s[0:1], xq, None, su[0:1], am[0:1], sat[0:1]),
-            lambda: fp8ds_cast(w, E4M3, s[1:2], wq, wqt, su[1:2], am[1:2], sat[1:2]),
-            lambda: fp8ds_gemm(OP_N, OP_T, M, N, K, xq, E4M3, K, su[0:1], wqt, E4M3, K, su[1:2], y,
-                               N, lin.amax_y, mma=lin.fwd_datapath(K)),
-            lambda: fp8ds_cast(dy, E5M2, s[2:3], dyq, None, su[2:3], am[2:3], sat[2:3]),
+            lambda: fp8ds_cast_acc(x, E4M3, s[0:1], xq, None, su[0:1], am[0:1], sat[0:1]),
+            lambda: fp8ds_cast_acc(w, E4M3, s[1:2], wq, wqt, su[1:2], am[1:2], sat[1:2]),
+            lambda: fp8ds_gemm_acc(OP_N, OP_T, M, N, K, xq, E4M3, K, su[0:1], wqt, E4M3, K, su[1:2],
+                                   y, N, amy, mma=lin.fwd_datapath(K)),
+            lambda: fp8ds_cast_acc(dy, E5M2, s[2:3], dyq, None, su[2:3], am[2:3], sat[2:3]),
             lambda: fp8ds_gemm(OP_N, OP_T, M, K, N, dyq, E5M2, N, su[2:3], wq, E4M3, N, su[1:2],
                                dx, K, mma=lin.mma_bwd),
-            lambda: fp8ds_gemm(OP_T, OP_N, K, N, M, xq, E4M3, K, su[0:1], dyq, E5M2, N, su[2:3],
-                               dw, N, lin.amax_dw, mma=lin.mma_bwd),
-            lambda: fp8ds_scale_update(lin.history, lin.cursor, am, lin.fmts, lin.algo, lin.margin,
-                                       s),
+            lambda: fp8ds_gemm_acc(OP_T, OP_N, K, N, M, xq, E4M3, K, su[0:1], dyq, E5M2, N,
+                                   su[2:3], dw, N, amdw, mma=lin.mma_bwd),
+            lambda: fp8ds_scale_update_clear(lin.history, lin.cursor, am, lin.fmts, lin.algo,
+                                             lin.margin, s, lin._acc[slot ^ 1]),
         ]
 
     def step(x, w, dy):
-        for fn in launches(x, w, dy):
-            fn()
+        lin.step(x, w, dy)
 
     for i in range(max(args.warmup, 1)):
         x, w, dy = sets[i % N_SETS]
@@ -560,7 +567,7 @@ def main():
     # would add several microseconds to every interval).  The scaling state is
     # restored afterwards.
     print(f"[bench] per-kernel timing, {args.steps} launches each", file=sys.stderr, flush=True)
-    saved = [t.clone() for t in (lin.history, lin.cursor, lin.scale)]
+    saved = [t.clone() for t in (lin.history, lin.cursor, lin.scale, lin._acc)]
     per = {}
     for j, name in enumerate(names):
         fns = [launches(*sets[i])[j] for i in range(N_SETS)]
@@ -574,7 +581,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         per[name] = e0.elapsed_time(e1) / args.steps
-    for t, v in zip((lin.history, lin.cursor, lin.scale), saved):
+    for t, v in zip((lin.history, lin.cursor, lin.scale, lin._acc), saved):
         t.copy_(v)
     torch.cuda.synchronize()
 
@@ -653,7 +660,7 @@ def main():
             "peak_f16_mfma": PEAK_F16_TFLOPS,
             "frac_f16_mfma": round(achieved / PEAK_F16_TFLOPS, 4),
         },
-        # the Linear's X cast: one fp8ds_cast call (reset kernel + cast kernel)
+        # the Linear's X cast: one fp8ds_cast_acc call (the cast kernel alone)
         "cast_roofline_linear": {
             "kernel": "cast_x",
             "bound": "hbm",

@@ -53,6 +53,14 @@ def _declare(lib):
     lib.fp8ds_amax.argtypes = [vp, i32, i64, vp, vp]
     lib.fp8ds_cast.restype = i32
     lib.fp8ds_cast.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.fp8ds_cast_acc.restype = i32
+    lib.fp8ds_cast_acc.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.fp8ds_scale_update_clear.restype = i32
+    lib.fp8ds_scale_update_clear.argtypes = [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, i64,
+                                             vp]
+    lib.fp8ds_gemm_acc.restype = i32
+    lib.fp8ds_gemm_acc.argtypes = [i32, i32, i64, i64, i64, vp, i32, i64, vp, vp, i32, i64, vp, vp,
+                                   i32, i64, vp, i32, vp]
     lib.fp8ds_cast_health.restype = i32
     lib.fp8ds_cast_health.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.fp8ds_cast_batched.restype = i32
@@ -192,6 +200,25 @@ def fp8ds_cast(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_count
                             _stream(stream)))
 
 
+def fp8ds_cast_acc(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_count=None,
+                   stream=None):
+    """:func:`fp8ds_cast` that max-/add-accumulates into ``amax`` / ``sat_count``."""
+    import torch
+
+    rows, cols = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.numel())
+    f32 = (torch.float32,)
+    _need(x, "x", (torch.bfloat16, torch.float32), 0)
+    _need(q, "q", (torch.uint8,), rows * cols)
+    _need(q_t, "q_t", (torch.uint8,), rows * cols)
+    _need(scale, "scale", f32, 1)
+    _need(scale_used, "scale_used", f32, 1)
+    _need(amax, "amax", f32, 1)
+    _need(sat_count, "sat_count", (torch.int64,), 1)
+    _check(lib().fp8ds_cast_acc(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
+                                _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(sat_count),
+                                _stream(stream)))
+
+
 HEALTH_COUNTS = 5
 HEALTH_NAMES = ("saturated", "nan", "inf", "zero", "near_max")
 
@@ -264,6 +291,30 @@ def fp8ds_scale_update(history, cursor, amax, fmts, algo, margin, scale, scale_i
                                     _ptr(scale_inv), _stream(stream)))
 
 
+def fp8ds_scale_update_clear(history, cursor, amax, fmts, algo, margin, scale, clear,
+                             scale_inv=None, stream=None):
+    """:func:`fp8ds_scale_update` that also zeroes the device tensor ``clear`` (the
+    next step's accumulators; contiguous, 4-byte elements or wider)."""
+    import torch
+
+    n, L = history.shape
+    if len(fmts) < n:
+        raise ValueError(f"fmts: {len(fmts)} formats for {n} tensors")
+    f32 = (torch.float32,)
+    _need(history, "history", f32, n * L)
+    _need(cursor, "cursor", (torch.int32,), n)
+    _need(amax, "amax", f32, n)
+    _need(scale, "scale", f32, n)
+    _need(scale_inv, "scale_inv", f32, n)
+    if not clear.is_cuda or not clear.is_contiguous():
+        raise ValueError("clear: expected a contiguous CUDA tensor")
+    arr = (ctypes.c_int * n)(*[int(f) for f in fmts[:n]])
+    _check(lib().fp8ds_scale_update_clear(n, L, _ptr(history), _ptr(cursor), _ptr(amax),
+                                          ctypes.cast(arr, ctypes.c_void_p), algo, margin,
+                                          _ptr(scale), _ptr(scale_inv), _ptr(clear),
+                                          clear.numel() * clear.element_size(), _stream(stream)))
+
+
 def _check_gemm(opa, opb, M, N, K, batch, a, lda, stride_a, scale_a, b, ldb, stride_b, scale_b, c,
                 ldc, stride_c, amax_c):
     """Tensor arguments cover the matrices the C call will address (the C ABI
@@ -294,6 +345,15 @@ def fp8ds_gemm(opa, opb, M, N, K, a, fa, lda, scale_a, b, fb, ldb, scale_b, c, l
     _check(lib().fp8ds_gemm(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_a), _ptr(b), fb, ldb,
                             _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c), mma,
                             _stream(stream)))
+
+
+def fp8ds_gemm_acc(opa, opb, M, N, K, a, fa, lda, scale_a, b, fb, ldb, scale_b, c, ldc,
+                   amax_c=None, stream=None, mma=MMA_EXACT):
+    """:func:`fp8ds_gemm` that max-accumulates the output amax into ``amax_c``."""
+    _check_gemm(opa, opb, M, N, K, 1, a, lda, 0, scale_a, b, ldb, 0, scale_b, c, ldc, 0, amax_c)
+    _check(lib().fp8ds_gemm_acc(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_a), _ptr(b), fb,
+                                ldb, _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c),
+                                mma, _stream(stream)))
 
 
 def fp8ds_gemm_batched(opa, opb, M, N, K, batch, a, fa, lda, stride_a, scale_a, b, fb, ldb,

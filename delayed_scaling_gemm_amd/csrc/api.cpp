@@ -94,10 +94,12 @@ int fp8ds_amax(const void* x, fp8ds_dtype xt, int64_t n, float* amax, hipStream_
   return hip_status(e, "fp8ds_amax");
 }
 
+// acc: amax / sat_count are combined into (max / add) instead of reset, and the
+// cast kernel writes scale_used itself: no reset kernel before the cast.
 static int cast_common(const char* who, const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols,
                        fp8ds_format fmt, const float* scale, uint8_t* q, uint8_t* q_t,
                        float* scale_used, float* amax, uint64_t* sat_count, uint64_t* health,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool acc = false) {
   if (!scale) return fail(FP8DS_ERR_NULL, "%s: scale is null", who);
   if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "%s: bad dtype %d", who, (int)xt);
   if (!valid_fmt(fmt)) return fail(FP8DS_ERR_ENUM, "%s: bad format %d", who, (int)fmt);
@@ -113,16 +115,20 @@ static int cast_common(const char* who, const void* x, fp8ds_dtype xt, int64_t r
   if (q_t && (rows + 127) / 128 > 65535)
     return fail(FP8DS_ERR_SHAPE, "%s: a transposed copy supports at most %d rows", who,
                 65535 * 128);
-  // with health counts, sat_count is counts[0] and the four others follow it
-  hipError_t e = fp8ds::launch_prologue(1, scale, scale_used, amax, sat_count, stream,
-                                        health ? FP8DS_HEALTH_COUNTS : 1);
+  hipError_t e = hipSuccess;
+  if (!acc)  // with health counts, sat_count is counts[0] and the four others follow it
+    e = fp8ds::launch_prologue(1, scale, scale_used, amax, sat_count, stream,
+                               health ? FP8DS_HEALTH_COUNTS : 1);
+  else if (n == 0)  // nothing to combine; the snapshot is still written
+    e = fp8ds::launch_prologue(1, scale, scale_used, nullptr, nullptr, stream);
+  float* snap = acc ? scale_used : nullptr;
   if (e == hipSuccess && n > 0) {
     if (q_t)
       e = fp8ds::launch_cast_transpose(x, xt == FP8DS_BF16, rows, cols, (int)fmt, scale, q, q_t,
-                                       amax, sat_count, health, stream);
+                                       amax, sat_count, health, stream, snap);
     else
       e = fp8ds::launch_cast(x, xt == FP8DS_BF16, 1, n, n, (int)fmt, scale, q, n, amax, sat_count,
-                             health, num_cus(), stream);
+                             health, num_cus(), stream, snap);
   }
   return hip_status(e, who);
 }
@@ -132,6 +138,13 @@ int fp8ds_cast(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_
                uint64_t* sat_count, hipStream_t stream) {
   return cast_common("fp8ds_cast", x, xt, rows, cols, fmt, scale, q, q_t, scale_used, amax,
                      sat_count, nullptr, stream);
+}
+
+int fp8ds_cast_acc(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+                   const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
+                   uint64_t* sat_count, hipStream_t stream) {
+  return cast_common("fp8ds_cast_acc", x, xt, rows, cols, fmt, scale, q, q_t, scale_used, amax,
+                     sat_count, nullptr, stream, true);
 }
 
 int fp8ds_cast_health(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
@@ -167,30 +180,65 @@ int fp8ds_cast_batched(const void* x, fp8ds_dtype xt, int64_t batch, int64_t n, 
                     "fp8ds_cast_batched");
 }
 
+static int scale_update_common(const char* who, int n_tensors, int hist_len, float* history,
+                               int32_t* cursor, const float* amax, const fp8ds_format* fmt,
+                               fp8ds_algo algo, int margin, float* scale, float* scale_inv,
+                               void* clear, int64_t clear_bytes, hipStream_t stream);
+
 int fp8ds_scale_update(int n_tensors, int hist_len, float* history, int32_t* cursor,
                        const float* amax, const fp8ds_format* fmt, fp8ds_algo algo, int margin,
                        float* scale, float* scale_inv, hipStream_t stream) {
+  return scale_update_common("fp8ds_scale_update", n_tensors, hist_len, history, cursor, amax,
+                             fmt, algo, margin, scale, scale_inv, nullptr, 0, stream);
+}
+
+int fp8ds_scale_update_clear(int n_tensors, int hist_len, float* history, int32_t* cursor,
+                             const float* amax, const fp8ds_format* fmt, fp8ds_algo algo,
+                             int margin, float* scale, float* scale_inv, void* clear,
+                             int64_t clear_bytes, hipStream_t stream) {
+  const char* who = "fp8ds_scale_update_clear";
+  if (clear_bytes < 0 || clear_bytes % 4 || clear_bytes > (int64_t(1) << 30))
+    return fail(FP8DS_ERR_SHAPE, "%s: clear_bytes %lld must be a multiple of 4 in [0, 2^30]", who,
+                (long long)clear_bytes);
+  if (clear_bytes > 0 && !clear) return fail(FP8DS_ERR_NULL, "%s: clear is null", who);
+  if (clear && (reinterpret_cast<uintptr_t>(clear) & 3u))
+    return fail(FP8DS_ERR_ALIGN, "%s: clear must be 4-byte aligned", who);
+  if (clear && amax && n_tensors > 0) {
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(clear), c1 = c0 + (uintptr_t)clear_bytes;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(amax), a1 = a0 + 4u * (uintptr_t)n_tensors;
+    if (c0 < a1 && a0 < c1)
+      return fail(FP8DS_ERR_VALUE, "%s: the cleared bytes overlap the amax being consumed", who);
+  }
+  return scale_update_common(who, n_tensors, hist_len, history, cursor, amax, fmt, algo, margin,
+                             scale, scale_inv, clear, clear_bytes, stream);
+}
+
+static int scale_update_common(const char* who, int n_tensors, int hist_len, float* history,
+                               int32_t* cursor, const float* amax, const fp8ds_format* fmt,
+                               fp8ds_algo algo, int margin, float* scale, float* scale_inv,
+                               void* clear, int64_t clear_bytes, hipStream_t stream) {
   if (n_tensors < 1 || n_tensors > 4096)
-    return fail(FP8DS_ERR_SHAPE, "fp8ds_scale_update: n_tensors %d not in [1, 4096]", n_tensors);
+    return fail(FP8DS_ERR_SHAPE, "%s: n_tensors %d not in [1, 4096]", who, n_tensors);
   if (hist_len < 1 || hist_len > 65536)
-    return fail(FP8DS_ERR_SHAPE, "fp8ds_scale_update: hist_len %d not in [1, 65536]", hist_len);
+    return fail(FP8DS_ERR_SHAPE, "%s: hist_len %d not in [1, 65536]", who, hist_len);
   if (!history || !cursor || !amax || !fmt || !scale)
-    return fail(FP8DS_ERR_NULL, "fp8ds_scale_update: history, cursor, amax, fmt and scale are "
-                                "required");
+    return fail(FP8DS_ERR_NULL, "%s: history, cursor, amax, fmt and scale are "
+                                "required", who);
   if (algo != FP8DS_ALGO_MAX && algo != FP8DS_ALGO_MOST_RECENT)
-    return fail(FP8DS_ERR_ENUM, "fp8ds_scale_update: bad algo %d", (int)algo);
+    return fail(FP8DS_ERR_ENUM, "%s: bad algo %d", who, (int)algo);
   if (margin < -126 || margin > 126)
-    return fail(FP8DS_ERR_SHAPE, "fp8ds_scale_update: margin %d not in [-126, 126]", margin);
+    return fail(FP8DS_ERR_SHAPE, "%s: margin %d not in [-126, 126]", who, margin);
   fp8ds::FmtBits bits;
   std::memset(&bits, 0, sizeof(bits));
   for (int t = 0; t < n_tensors; ++t) {
     if (!valid_fmt(fmt[t]))
-      return fail(FP8DS_ERR_ENUM, "fp8ds_scale_update: bad format %d for tensor %d", (int)fmt[t], t);
+      return fail(FP8DS_ERR_ENUM, "%s: bad format %d for tensor %d", who, (int)fmt[t], t);
     if (fmt[t] == FP8DS_E5M2) bits.w[t >> 5] |= 1u << (t & 31);
   }
   return hip_status(fp8ds::launch_scale_update(n_tensors, hist_len, history, cursor, amax, bits,
-                                               (int)algo, margin, scale, scale_inv, stream),
-                    "fp8ds_scale_update");
+                                               (int)algo, margin, scale, scale_inv, stream,
+                                               static_cast<uint32_t*>(clear), clear_bytes / 4),
+                    who);
 }
 
 static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N,
@@ -198,7 +246,8 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
                        int64_t stride_a, const float* scale_a, const uint8_t* B, fp8ds_format fb,
                        int64_t ldb, int64_t stride_b, const float* scale_b, void* C,
                        fp8ds_dtype ct, int64_t ldc, int64_t stride_c, float* amax_c,
-                       fp8ds_mma mma, hipStream_t stream, bool rowcol = false) {
+                       fp8ds_mma mma, hipStream_t stream, bool rowcol = false,
+                       bool reset = true) {
   // rowcol: scale_a / scale_b are inverse-scale vectors [M] / [N] (exact datapath)
   if (mma != FP8DS_MMA_EXACT && mma != FP8DS_MMA_FP8)
     return fail(FP8DS_ERR_ENUM, "%s: bad mma %d", who, (int)mma);
@@ -218,7 +267,7 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
     return fail(FP8DS_ERR_SHAPE, "%s: M x N %lld x %lld has too many tiles", who, (long long)M,
                 (long long)N);
   if (M == 0 || N == 0 || batch == 0) {
-    if (amax_c && batch > 0)
+    if (amax_c && batch > 0 && reset)
       return hip_status(fp8ds::launch_prologue(batch, nullptr, nullptr, amax_c, nullptr, stream),
                         who);
     return ok();
@@ -243,7 +292,7 @@ static int gemm_common(const char* who, fp8ds_op opa, fp8ds_op opb, int64_t M, i
                     stride_b < 0 || stride_c < 0))
     return fail(FP8DS_ERR_ALIGN, "%s: batch strides must keep 16-byte alignment", who);
   hipError_t e = hipSuccess;
-  if (amax_c) e = fp8ds::launch_prologue(batch, nullptr, nullptr, amax_c, nullptr, stream);
+  if (amax_c && reset) e = fp8ds::launch_prologue(batch, nullptr, nullptr, amax_c, nullptr, stream);
   if (e == hipSuccess) {
     fp8ds::GemmProblem p;
     p.opa = (int)opa; p.opb = (int)opb;
@@ -270,6 +319,14 @@ int fp8ds_gemm(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K, cons
                int64_t ldc, float* amax_c, fp8ds_mma mma, hipStream_t stream) {
   return gemm_common("fp8ds_gemm", opa, opb, M, N, K, 1, A, fa, lda, 0, scale_a, B, fb, ldb, 0,
                      scale_b, C, ct, ldc, 0, amax_c, mma, stream);
+}
+
+int fp8ds_gemm_acc(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                   fp8ds_format fa, int64_t lda, const float* scale_a, const uint8_t* B,
+                   fp8ds_format fb, int64_t ldb, const float* scale_b, void* C, fp8ds_dtype ct,
+                   int64_t ldc, float* amax_c, fp8ds_mma mma, hipStream_t stream) {
+  return gemm_common("fp8ds_gemm_acc", opa, opb, M, N, K, 1, A, fa, lda, 0, scale_a, B, fb, ldb, 0,
+                     scale_b, C, ct, ldc, 0, amax_c, mma, stream, false, false);
 }
 
 int fp8ds_gemm_batched(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K, int64_t batch,

@@ -49,9 +49,10 @@ struct CastArgs {
   uint32_t* amax;     // [batch] or null
   unsigned long long* sat;  // [batch] or null
   unsigned long long* health;  // [batch][4] NaN, Inf, zero, near-max counts (STATS)
-  float* scale_used;  // [batch] or null: written only with `direct`
-  int direct;         // one workgroup per tensor: it stores amax, saturation count
-                      // and the scale snapshot itself (no prologue kernel)
+  float* scale_used;  // [batch] or null: the scale snapshot, written by the first
+                      // workgroup of each tensor (no prologue kernel)
+  int direct;         // one workgroup per tensor: it stores amax and saturation count
+                      // itself instead of combining them atomically
 };
 
 // Each workgroup of T threads owns the contiguous range of T * kGroups * 16
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(TH) void cast_kernel(CastArgs p) {
   Health h;
   const int b = blockIdx.y;
   const float s = WRITE_Q ? p.scale[b] : 1.0f;
-  if (WRITE_Q && p.direct && p.scale_used && threadIdx.x == 0) p.scale_used[b] = s;
+  if (WRITE_Q && p.scale_used && blockIdx.x == 0 && threadIdx.x == 0) p.scale_used[b] = s;
   const bool want_sat = WRITE_Q && p.sat != nullptr;
   const int64_t n = p.n;
   const int64_t npieces = n / PER;
@@ -208,7 +209,8 @@ template <bool BF16, int FMT, bool STATS>
 __global__ __launch_bounds__(256) void cast_transpose_kernel(
     const void* __restrict__ xp, int64_t rows, int64_t cols, const float* __restrict__ scale,
     uint8_t* __restrict__ q, uint8_t* __restrict__ qt, uint32_t* __restrict__ g_amax,
-    unsigned long long* __restrict__ g_sat, unsigned long long* __restrict__ g_health) {
+    unsigned long long* __restrict__ g_sat, unsigned long long* __restrict__ g_health,
+    float* __restrict__ scale_used) {
   constexpr int T = 128;
   __shared__ __attribute__((aligned(16))) uint8_t tile[T * T];
   __shared__ uint32_t red[(STATS ? 6 : 2) * 4];
@@ -216,6 +218,7 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(
   const float s = scale[0];
   const int64_t c0 = (int64_t)blockIdx.x * T;
   const int tid = threadIdx.x;
+  if (scale_used && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) scale_used[0] = s;
   uint32_t amax = 0, sat = 0;
   for (int ti = 0; ti < kTransposeTiles; ++ti) {
     const int64_t r0 = ((int64_t)blockIdx.y * kTransposeTiles + ti) * T;
@@ -363,11 +366,12 @@ static hipError_t launch_cast_f(const CastArgs& a, int fmt, int64_t batch, hipSt
 
 hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride_x,
                        int fmt, const float* scale, uint8_t* q, int64_t stride_q, float* amax,
-                       uint64_t* sat, uint64_t* health, int num_cus, hipStream_t stream) {
+                       uint64_t* sat, uint64_t* health, int num_cus, hipStream_t stream,
+                       float* scale_used) {
   (void)num_cus;
   CastArgs a{x, n, stride_x, scale, q, stride_q, reinterpret_cast<uint32_t*>(amax),
              reinterpret_cast<unsigned long long*>(sat),
-             reinterpret_cast<unsigned long long*>(health)};
+             reinterpret_cast<unsigned long long*>(health), q ? scale_used : nullptr, 0};
   if (q == nullptr) {
     return bf16 ? launch_cast_t<true, kE4M3, false, false>(a, batch, stream)
                 : launch_cast_t<false, kE4M3, false, false>(a, batch, stream);
@@ -408,11 +412,12 @@ hipError_t launch_cast_batched(const void* x, bool bf16, int64_t batch, int64_t 
 template <bool BF16, int FMT, bool STATS>
 static hipError_t launch_transpose_t(dim3 grid, const void* x, int64_t rows, int64_t cols,
                                      const float* scale, uint8_t* q, uint8_t* qt, float* amax,
-                                     uint64_t* sat, uint64_t* health, hipStream_t stream) {
+                                     uint64_t* sat, uint64_t* health, float* scale_used,
+                                     hipStream_t stream) {
   hipLaunchKernelGGL((cast_transpose_kernel<BF16, FMT, STATS>), grid, dim3(256), 0, stream, x,
                      rows, cols, scale, q, qt, reinterpret_cast<uint32_t*>(amax),
                      reinterpret_cast<unsigned long long*>(sat),
-                     reinterpret_cast<unsigned long long*>(health));
+                     reinterpret_cast<unsigned long long*>(health), scale_used);
   return hipGetLastError();
 }
 
@@ -420,30 +425,31 @@ template <bool STATS>
 static hipError_t launch_transpose_s(dim3 grid, const void* x, bool bf16, int64_t rows,
                                      int64_t cols, int fmt, const float* scale, uint8_t* q,
                                      uint8_t* qt, float* amax, uint64_t* sat, uint64_t* health,
-                                     hipStream_t stream) {
+                                     float* scale_used, hipStream_t stream) {
   if (bf16)
     return fmt == kE4M3
                ? launch_transpose_t<true, kE4M3, STATS>(grid, x, rows, cols, scale, q, qt, amax,
-                                                        sat, health, stream)
+                                                        sat, health, scale_used, stream)
                : launch_transpose_t<true, kE5M2, STATS>(grid, x, rows, cols, scale, q, qt, amax,
-                                                        sat, health, stream);
+                                                        sat, health, scale_used, stream);
   return fmt == kE4M3
              ? launch_transpose_t<false, kE4M3, STATS>(grid, x, rows, cols, scale, q, qt, amax, sat,
-                                                       health, stream)
+                                                       health, scale_used, stream)
              : launch_transpose_t<false, kE5M2, STATS>(grid, x, rows, cols, scale, q, qt, amax, sat,
-                                                       health, stream);
+                                                       health, scale_used, stream);
 }
 
 hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
                                  const float* scale, uint8_t* q, uint8_t* qt, float* amax,
-                                 uint64_t* sat, uint64_t* health, hipStream_t stream) {
+                                 uint64_t* sat, uint64_t* health, hipStream_t stream,
+                                 float* scale_used) {
   dim3 grid((unsigned)((cols + 127) / 128),
             (unsigned)(((rows + 127) / 128 + kTransposeTiles - 1) / kTransposeTiles));
   if (health)
     return launch_transpose_s<true>(grid, x, bf16, rows, cols, fmt, scale, q, qt, amax, sat,
-                                    health, stream);
+                                    health, scale_used, stream);
   return launch_transpose_s<false>(grid, x, bf16, rows, cols, fmt, scale, q, qt, amax, sat,
-                                   nullptr, stream);
+                                   nullptr, scale_used, stream);
 }
 
 }  // namespace fp8ds

@@ -14,11 +14,14 @@ hipError_t launch_prologue(int64_t count, const float* scale, float* scale_used,
                            uint64_t* sat, hipStream_t stream, int counters = 1);
 
 // Fused amax + cast over `batch` tensors of n elements (q == nullptr: amax only).
-// amax, sat and health must have been reset by launch_prologue.  health (or null):
-// [batch][4] counts of NaN inputs, infinite inputs, zero codes and top-binade codes.
+// amax, sat and health are combined into (max / add): reset them first
+// (launch_prologue) unless accumulating.  health (or null): [batch][4] counts of
+// NaN inputs, infinite inputs, zero codes and top-binade codes.  scale_used (or
+// null): [batch] scale snapshots, written by the cast kernel.
 hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride_x,
                        int fmt, const float* scale, uint8_t* q, int64_t stride_q, float* amax,
-                       uint64_t* sat, uint64_t* health, int num_cus, hipStream_t stream);
+                       uint64_t* sat, uint64_t* health, int num_cus, hipStream_t stream,
+                       float* scale_used = nullptr);
 // Batched cast with its output resets and scale snapshot (scale_used, amax, sat:
 // [batch] or null), taken by the cast kernel itself where one workgroup covers a
 // tensor, else by the prologue kernel.
@@ -27,10 +30,12 @@ hipError_t launch_cast_batched(const void* x, bool bf16, int64_t batch, int64_t 
                                int64_t stride_q, float* scale_used, float* amax, uint64_t* sat,
                                hipStream_t stream);
 
-// Cast of a [rows x cols] tensor writing q and its transpose qt (health as above).
+// Cast of a [rows x cols] tensor writing q and its transpose qt (health and
+// scale_used as above).
 hipError_t launch_cast_transpose(const void* x, bool bf16, int64_t rows, int64_t cols, int fmt,
                                  const float* scale, uint8_t* q, uint8_t* qt, float* amax,
-                                 uint64_t* sat, uint64_t* health, hipStream_t stream);
+                                 uint64_t* sat, uint64_t* health, hipStream_t stream,
+                                 float* scale_used = nullptr);
 
 // Fused AdamW step + FP8 cast of the updated weights.  The per-step fp32
 // constants are derived on the host from the hyperparameters and the step count.
@@ -74,9 +79,12 @@ hipError_t launch_current_scale(const float* amax, int fmt, int margin, float* s
 struct FmtBits {
   uint32_t w[128];
 };
+// clear (or null): n_clear 32-bit words zeroed by the same kernel (the next
+// step's accumulators; must not overlap the other arguments).
 hipError_t launch_scale_update(int n, int hist_len, float* history, int32_t* cursor,
                                const float* amax, const FmtBits& fmt, int algo, int margin,
-                               float* scale, float* scale_inv, hipStream_t stream);
+                               float* scale, float* scale_inv, hipStream_t stream,
+                               uint32_t* clear = nullptr, int64_t n_clear = 0);
 
 // FP8 GEMM.  opa/opb: 0 = N, 1 = T.  out_bf16: BF16 output, else FP32.
 struct GemmProblem {

@@ -6,7 +6,9 @@
 // the cursor, the cursor advances modulo the history length, and the scale falls
 // back to 1.0 when the window maximum is not positive.
 //
-// One wave per tensor.  The window (up to 65536 fp32) is read with a stride of 64
+// One wave per tensor.  Optionally the same launch zeroes a caller buffer: the
+// accumulators the next step's casts and GEMMs combine into, so that no reset
+// kernel runs before them.  The window (up to 65536 fp32) is read with a stride of 64
 // lanes; the slot being overwritten takes the new amax in registers, so no lane
 // depends on another lane's store.  The max tracks NaN separately so that the
 // result is NaN whenever any entry is, whatever the entries' signs.
@@ -22,10 +24,14 @@ __global__ __launch_bounds__(64) void scale_update_kernel(int n, int hist_len,
                                                           const float* __restrict__ amax, FmtBits fmt,
                                                           int algo, int margin,
                                                           float* __restrict__ scale,
-                                                          float* __restrict__ scale_inv) {
+                                                          float* __restrict__ scale_inv,
+                                                          uint32_t* __restrict__ clear,
+                                                          int64_t n_clear) {
   const int t = blockIdx.x;
   if (t >= n) return;
   const int lane = threadIdx.x;
+  // the next step's accumulators, spread over the blocks
+  for (int64_t i = (int64_t)t * 64 + lane; i < n_clear; i += (int64_t)n * 64) clear[i] = 0u;
   float* h = history + (int64_t)t * hist_len;
   // The cursor is caller state in device memory; reduce it modulo the history
   // length so that a corrupted value can never address outside this history.
@@ -60,10 +66,12 @@ __global__ __launch_bounds__(64) void scale_update_kernel(int n, int hist_len,
 
 hipError_t launch_scale_update(int n, int hist_len, float* history, int32_t* cursor,
                                const float* amax, const FmtBits& fmt, int algo, int margin,
-                               float* scale, float* scale_inv, hipStream_t stream) {
+                               float* scale, float* scale_inv, hipStream_t stream,
+                               uint32_t* clear, int64_t n_clear) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(scale_update_kernel, dim3(n), dim3(64), 0, stream, n, hist_len, history,
-                     cursor, amax, fmt, algo, margin, scale, scale_inv);
+                     cursor, amax, fmt, algo, margin, scale, scale_inv, clear,
+                     clear ? n_clear : 0);
   return hipGetLastError();
 }
 

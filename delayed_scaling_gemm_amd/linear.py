@@ -9,6 +9,8 @@ Host-side orchestration only (every arithmetic step runs in the HIP library):
         dX = dYq . Wq^T      (NT)             -> BF16 dX           (exact F16-widened path)
         dW = Xq^T . dYq      (TN)             -> BF16 dW           (exact F16-widened path)
   end:  one scale update over the X, W, dY histories -> scales of the next step
+        (the same launch zeroes the accumulators the next step's casts and
+        GEMMs combine into, so the step runs no reset kernels)
   opt:  (optional) adamw_step: fused AdamW on the fp32 master weights with this
         step's dW, writing Wq, Wq^T, amax_W and the W scale snapshot of the next
         step, whose forward then skips the W cast
@@ -31,8 +33,8 @@ from __future__ import annotations
 import torch
 
 from . import (ALGO_MAX, E4M3, E5M2, HEALTH_COUNTS, HEALTH_NAMES, MMA_EXACT, MMA_FP8, OP_N, OP_T,
-               fp8ds_adamw, fp8ds_cast, fp8ds_cast_health, fp8ds_cast_mx, fp8ds_gemm,
-               fp8ds_gemm_mx, fp8ds_scale_update)
+               fp8ds_adamw, fp8ds_cast_acc, fp8ds_cast_health, fp8ds_cast_mx, fp8ds_gemm,
+               fp8ds_gemm_acc, fp8ds_gemm_mx, fp8ds_scale_update, fp8ds_scale_update_clear)
 
 X, W, DY = 0, 1, 2
 # shortest forward reduction that runs on the FP8 matrix instructions by default
@@ -76,10 +78,14 @@ class DelayedScalingLinear:
         self.cursor = torch.zeros(3, dtype=torch.int32, device=self.device)
         self.scale = torch.ones(3, **f32)
         self.scale_used = torch.zeros(3, **f32)
-        self.amax = torch.zeros(3, **f32)
-        self.sat = torch.zeros(3, dtype=torch.int64, device=self.device)
-        self.amax_y = torch.zeros(1, **f32)
-        self.amax_dw = torch.zeros(1, **f32)  # fused output amax of dW (skip rule)
+        # Per-step accumulators, two sets used on alternate steps: the casts and
+        # GEMMs of step t combine into set t % 2 (fp8ds_cast_acc, fp8ds_gemm_acc),
+        # and the scale update that ends step t zeroes set (t + 1) % 2 for the
+        # next step, so no reset kernel runs inside a step and step t's values
+        # stay readable until the end of step t + 1.  Words of a set: amax of X,
+        # W, dY (fp32) at 0..2, amax of Y at 3, of dW at 4, saturation counts
+        # of X, W, dY (int64) at 8..13.
+        self._acc = torch.zeros(2, 16, dtype=torch.int32, device=self.device)
         self._w_prepared = None  # master weights whose FP8 copy adamw_step wrote
         self.w_counts_valid = True
         # health=True: each cast also counts saturated, NaN, Inf, zero and
@@ -88,15 +94,49 @@ class DelayedScalingLinear:
                        if health else None)
         self._bufs = {}
 
+    # views of an accumulator set
+    def _amax_of(self, slot):
+        return self._acc[slot, 0:3].view(torch.float32)
+
+    def _sat_of(self, slot):
+        return self._acc[slot, 8:14].view(torch.int64)
+
+    @property
+    def _slot(self):
+        """The accumulator set of the step that runs next."""
+        return self.steps & 1
+
+    @property
+    def amax(self):
+        """amax of X, W and dY of the last step (fp32 [3], device)."""
+        return self._amax_of((self.steps - 1) & 1)
+
+    @property
+    def sat(self):
+        """Saturation counts of the last step's casts (int64 [3], device)."""
+        return self._sat_of((self.steps - 1) & 1)
+
+    @property
+    def amax_y(self):
+        """Fused output amax of the last step's forward GEMM (fp32 [1], device)."""
+        return self._acc[(self.steps - 1) & 1, 3:4].view(torch.float32)
+
+    @property
+    def amax_dw(self):
+        """Fused output amax of the last step's dW GEMM (fp32 [1], device; the
+        optimizer's skip rule)."""
+        return self._acc[(self.steps - 1) & 1, 4:5].view(torch.float32)
+
     def _cast(self, t, x, q, q_t, stream):
-        s, su, am = self.scale, self.scale_used, self.amax
+        s, su = self.scale, self.scale_used
+        am, sat = self._amax_of(self._slot), self._sat_of(self._slot)
         if self.health and self.steps % self.health_every == 0:
             self.health_step = self.steps
             fp8ds_cast_health(x, self.fmts[t], s[t:t + 1], q, self.counts[t], q_t, su[t:t + 1],
                               am[t:t + 1], stream)
         else:
-            fp8ds_cast(x, self.fmts[t], s[t:t + 1], q, q_t, su[t:t + 1], am[t:t + 1],
-                       self.sat[t:t + 1], stream)
+            fp8ds_cast_acc(x, self.fmts[t], s[t:t + 1], q, q_t, su[t:t + 1], am[t:t + 1],
+                           sat[t:t + 1], stream)
 
     def fwd_datapath(self, K: int) -> int:
         """The forward GEMM's datapath for a reduction of length K."""
@@ -170,7 +210,10 @@ class DelayedScalingLinear:
         wq = self._buf("wq", (K, N), u8)
         wqt = self._buf("wqt", (N, K), u8)
         y = self._buf("y", (M, N), torch.bfloat16)
-        s, su, am = self.scale, self.scale_used, self.amax
+        slot = self._slot
+        s, su, am = self.scale, self.scale_used, self._amax_of(slot)
+        amax_y = self._acc[slot, 3:4].view(torch.float32)
+        amax_dw = self._acc[slot, 4:5].view(torch.float32)
         self._cast(X, x, xq, None, stream)
         if self._w_prepared is not None and self._w_prepared is w:
             # adamw_step already wrote Wq, Wq^T, amax_W and the W snapshot
@@ -182,8 +225,8 @@ class DelayedScalingLinear:
             self._cast(W, w, wq, wqt, stream)
         self._w_prepared = None
         # Y[M, N] = Xq[M, K] . Wq[K, N], with Wq^T stored [N, K] -> op T
-        fp8ds_gemm(OP_N, OP_T, M, N, K, xq, self.fmts[X], K, su[X:X + 1], wqt, self.fmts[W], K,
-                   su[W:W + 1], y, N, self.amax_y, stream, mma=self.fwd_datapath(K))
+        fp8ds_gemm_acc(OP_N, OP_T, M, N, K, xq, self.fmts[X], K, su[X:X + 1], wqt, self.fmts[W],
+                       K, su[W:W + 1], y, N, amax_y, stream, mma=self.fwd_datapath(K))
         out = {"xq": xq, "wq": wq, "wqt": wqt, "y": y}
         n_upd = 2
         if dy is not None:
@@ -196,12 +239,15 @@ class DelayedScalingLinear:
             fp8ds_gemm(OP_N, OP_T, M, K, N, dyq, self.fmts[DY], N, su[DY:DY + 1], wq, self.fmts[W],
                        N, su[W:W + 1], dx, K, None, stream, mma=self.mma_bwd)
             # dW[K, N] = Xq^T . dYq         (Xq stored [M, K] = [K' x M'] -> op T)
-            fp8ds_gemm(OP_T, OP_N, K, N, M, xq, self.fmts[X], K, su[X:X + 1], dyq, self.fmts[DY],
-                       N, su[DY:DY + 1], dw, N, self.amax_dw, stream, mma=self.mma_bwd)
+            fp8ds_gemm_acc(OP_T, OP_N, K, N, M, xq, self.fmts[X], K, su[X:X + 1], dyq,
+                           self.fmts[DY], N, su[DY:DY + 1], dw, N, amax_dw, stream,
+                           mma=self.mma_bwd)
             out.update(dyq=dyq, dx=dx, dw=dw)
             n_upd = 3
-        fp8ds_scale_update(self.history[:n_upd], self.cursor[:n_upd], am[:n_upd],
-                           self.fmts[:n_upd], self.algo, self.margin, s[:n_upd], None, stream)
+        # the scale update also zeroes the next step's accumulator set
+        fp8ds_scale_update_clear(self.history[:n_upd], self.cursor[:n_upd], am[:n_upd],
+                                 self.fmts[:n_upd], self.algo, self.margin, s[:n_upd],
+                                 self._acc[slot ^ 1], None, stream)
         self.steps += 1
         return out
 
@@ -225,10 +271,12 @@ class DelayedScalingLinear:
         K, N = w.shape
         wq = self._buf("wq", (K, N), torch.uint8)
         wqt = self._buf("wqt", (N, K), torch.uint8)
-        s, su, am = self.scale, self.scale_used, self.amax
+        # the new weights' amax and saturation go into the next step's set
+        s, su = self.scale, self.scale_used
+        am, sat = self._amax_of(self._slot), self._sat_of(self._slot)
         fp8ds_adamw(w, dw, m, v, lr, beta1, beta2, eps, weight_decay, step, grad_scale=grad_scale,
                     grad_amax=self.amax_dw, fmt=self.fmts[W], scale=s[W:W + 1], q=wq, q_t=wqt,
-                    scale_used=su[W:W + 1], amax=am[W:W + 1], sat_count=self.sat[W:W + 1],
+                    scale_used=su[W:W + 1], amax=am[W:W + 1], sat_count=sat[W:W + 1],
                     stream=stream)
         self._w_prepared = w
 

@@ -33,7 +33,10 @@
  *     (amax = 0, saturation count = 0, scale_used = *scale).
  *   - Row-major layouts; `ld*` are leading dimensions in elements.
  *   - Calls that write the same output buffers must not overlap (the fused
- *     amax / counters are reset by the call that writes them).
+ *     amax / counters are reset by the call that writes them).  The `_acc`
+ *     variants (fp8ds_cast_acc, fp8ds_gemm_acc) combine into their amax and
+ *     counters instead; fp8ds_scale_update_clear zeroes such accumulators for
+ *     the next step, so a training step needs no reset launches.
  */
 #ifndef FP8DS_H
 #define FP8DS_H
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FP8DS_ABI_VERSION 6
+#define FP8DS_ABI_VERSION 7
 
 typedef enum {
   FP8DS_OK = 0,
@@ -144,6 +147,21 @@ int fp8ds_cast(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_
                uint64_t* sat_count, hipStream_t stream);
 
 /*
+ * fp8ds_cast_acc -- fp8ds_cast that accumulates its reductions instead of
+ * resetting them (same arguments, same bytes q / q_t):
+ *   amax       device or NULL: on return max(previous amax, max|x|) (fp32 bits of
+ *              non-negative values compared as integers; NaN as fp8ds_amax).
+ *   sat_count  device or NULL: the saturation count of this call added to it.
+ *   scale_used device or NULL: written by the cast kernel itself.
+ * With amax and sat_count zeroed before a step (fp8ds_scale_update_clear of the
+ * previous step does it), the results equal fp8ds_cast's, with no reset kernel
+ * launched before the cast.
+ */
+int fp8ds_cast_acc(const void* x, fp8ds_dtype xt, int64_t rows, int64_t cols, fp8ds_format fmt,
+                   const float* scale, uint8_t* q, uint8_t* q_t, float* scale_used, float* amax,
+                   uint64_t* sat_count, hipStream_t stream);
+
+/*
  * fp8ds_cast_health -- fp8ds_cast plus quantization-health counts of the same pass.
  * [P3] "第四步：建立 Amax 与低精度异常画像" (per-module metrics: the share of values
  * near the FP8 upper limit, the share of zeros after quantization, NaN / Inf /
@@ -214,6 +232,19 @@ int fp8ds_scale_update(int n_tensors, int hist_len, float* history, int32_t* cur
                        float* scale, float* scale_inv, hipStream_t stream);
 
 /*
+ * fp8ds_scale_update_clear -- fp8ds_scale_update that also zeroes `clear_bytes`
+ * bytes at `clear` (device, 4-byte aligned, a multiple of 4 bytes up to 2^30)
+ * in the same launch: the accumulators that the next step's fp8ds_cast_acc and
+ * fp8ds_gemm_acc calls combine into.  The cleared bytes must not overlap the
+ * other arguments (an overlap with amax returns FP8DS_ERR_VALUE); clear may be
+ * NULL when clear_bytes is 0.
+ */
+int fp8ds_scale_update_clear(int n_tensors, int hist_len, float* history, int32_t* cursor,
+                             const float* amax, const fp8ds_format* fmt, fp8ds_algo algo,
+                             int margin, float* scale, float* scale_inv, void* clear,
+                             int64_t clear_bytes, hipStream_t stream);
+
+/*
  * fp8ds_gemm -- C = dequant( op(A) . op(B) ), FP8 x FP8 with FP32 accumulation.
  * [P2] §五 (the fp8 linear op: FP8 product divided by the product of the two
  * scales; the per-tensor FP8 GEMM: FP8 inputs, FP32 accumulate, BF16 output);
@@ -243,6 +274,16 @@ int fp8ds_gemm(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K,
                const uint8_t* B, fp8ds_format fb, int64_t ldb, const float* scale_b,
                void* C, fp8ds_dtype ct, int64_t ldc, float* amax_c, fp8ds_mma mma,
                hipStream_t stream);
+
+/*
+ * fp8ds_gemm_acc -- fp8ds_gemm whose output amax is combined into amax_c
+ * (max(previous, max|C|)) instead of reset; otherwise identical.
+ */
+int fp8ds_gemm_acc(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t K,
+                   const uint8_t* A, fp8ds_format fa, int64_t lda, const float* scale_a,
+                   const uint8_t* B, fp8ds_format fb, int64_t ldb, const float* scale_b,
+                   void* C, fp8ds_dtype ct, int64_t ldc, float* amax_c, fp8ds_mma mma,
+                   hipStream_t stream);
 
 /*
  * fp8ds_gemm_batched -- `batch` independent GEMMs of one shape, each with its own

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     for n in ("fp8ds_amax", "fp8ds_cast", "fp8ds_cast_batched", "fp8ds_scale_update",
               "fp8ds_gemm", "fp8ds_gemm_batched", "fp8ds_status_string", "fp8ds_last_error",
               "fp8ds_abi_version", "fp8ds_adamw", "fp8ds_cast_health", "fp8ds_cast_rowwise",
-              "fp8ds_cast_current", "fp8ds_gemm_rowcol", "fp8ds_cast_mx", "fp8ds_gemm_mx"):
+              "fp8ds_cast_current", "fp8ds_gemm_rowcol", "fp8ds_cast_mx", "fp8ds_gemm_mx",
+              "fp8ds_cast_acc", "fp8ds_gemm_acc", "fp8ds_scale_update_clear"):
         assert n in names
 
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(dsg.LIB_PATH)
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert dsg.abi_version() == 6
+    assert dsg.abi_version() == 7
 
 
 def test_status_strings():
@@ -175,3 +176,25 @@ def test_mx_validation_errors_without_gpu():
     assert L.fp8ds_gemm_mx(64, 64, 256, p, 7, 256, p, 8, p, 0, 256, p, 8, p, 1, 64, None, 0,
                            None) == -3
     assert g(mma=5) == -3
+
+
+def test_accumulating_variants_validate_like_the_plain_calls():
+    """fp8ds_cast_acc and fp8ds_gemm_acc reject what fp8ds_cast and fp8ds_gemm
+    reject; fp8ds_scale_update_clear checks its clear range (CPU only)."""
+    L = dsg.lib()
+    p = 0x1000
+    assert L.fp8ds_cast_acc(p, 1, 4, 4, 0, None, p, None, None, None, None, None) == -1
+    assert L.fp8ds_cast_acc(p, 1, 4, 4, 5, p, p, None, None, None, None, None) == -3
+    assert L.fp8ds_cast_acc(p, 1, 4, 4, 0, p, p + 8, None, None, None, None, None) == -4
+    assert L.fp8ds_gemm_acc(1, 1, 64, 64, 64, p, 0, 64, p, p, 0, 64, p, p, 1, 64, None, 0,
+                            None) == -6
+    assert L.fp8ds_gemm_acc(0, 1, 64, 64, 64, p, 0, 32, p, p, 0, 64, p, p, 1, 64, None, 0,
+                            None) == -2
+    fm = (ctypes.c_int * 2)(0, 1)
+    fmp = ctypes.cast(fm, ctypes.c_void_p)
+    clr = L.fp8ds_scale_update_clear
+    assert clr(2, 16, p, p, p, fmp, 0, 0, p, None, p + 0x100, 6, None) == -2   # not a multiple of 4
+    assert clr(2, 16, p, p, p, fmp, 0, 0, p, None, None, 8, None) == -1        # clear is null
+    assert clr(2, 16, p, p, p, fmp, 0, 0, p, None, p + 0x102, 8, None) == -4   # misaligned
+    assert clr(2, 16, p, p, p, fmp, 0, 0, p, None, p + 4, 8, None) == -7       # overlaps amax
+    assert clr(0, 16, p, p, p, fmp, 0, 0, p, None, p + 0x100, 8, None) == -2   # as scale_update

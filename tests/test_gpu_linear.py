@@ -294,10 +294,12 @@ def test_fused_adamw_step_matches_the_unfused_loop():
         for k in ("scale", "history", "cursor"):  # as bits: the dY history holds a NaN
             assert torch.equal(getattr(a["lin"], k).view(torch.int32),
                                getattr(b["lin"], k).view(torch.int32)), (step, k)
-        # amax[W] of the fused run already describes the next step's weights (its
-        # push into the history is compared above, one step later)
+        # the fused run wrote the new weights' amax into the next step's
+        # accumulator set (its push into the history is compared above, one step
+        # later); the last step's amaxes of X and dY agree
         assert torch.equal(a["lin"].amax[0::2].view(torch.int32),
                            b["lin"].amax[0::2].view(torch.int32)), step
-        assert b["lin"].amax[1].item() == b["w"].abs().max().item()
+        lb = b["lin"]
+        assert lb._amax_of(lb._slot)[1].item() == b["w"].abs().max().item()
     # the fused run cast W only in its first forward
     assert w_casts.count(1) == 1
