@@ -292,3 +292,26 @@ def test_large_ragged_cast(bf16):
                                     np.flatnonzero(x == 1000.0)]))
     codes, _ = ofp8.cast(get(pos), np.float32(scale), dsg.E4M3)
     assert np.array_equal(q[pos], codes)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("n", [(1 << 22) + 12345, (1 << 23) + 7])
+def test_large_ragged_tensor_every_byte(fmt, bf16, n):
+    """Single tensors from 2^22 elements on take the persistent cast (chunks walked
+    by about two workgroups per CU): every byte, the amax and the saturation count
+    of a ragged length (partial last chunk, partial groups, a tail below one
+    16-byte piece) against the oracle."""
+    rng = np.random.default_rng(n + 2 * fmt + int(bf16))
+    x32 = (rng.standard_normal(n) * 3.0).astype(np.float32)
+    x32[rng.choice(n, 101, replace=False)] = 7.0e4  # saturate both formats
+    if bf16:
+        bits = (x32.view(np.uint32) >> 16).astype(np.uint16)  # truncated to bf16, any pattern
+        x_dev, xw = dev_bf16(bits), obf16.widen(bits)
+    else:
+        x_dev, xw = dev_f32(x32), x32
+    s = np.float32(448.0) / np.float32(3.7)
+    q, _, su, am, sat = run_cast(x_dev, fmt, s)
+    codes, oa, osat = oracle_cast(xw, fmt, s)
+    assert np.array_equal(q, codes)
+    assert am == oa and sat == osat and su == np.float32(s)
