@@ -8,7 +8,7 @@ built or cannot be loaded, every call raises.
 
 Functions keep the C names: ``fp8ds_amax``, ``fp8ds_cast``, ``fp8ds_cast_health``,
 ``fp8ds_cast_batched``, ``fp8ds_scale_update``, ``fp8ds_gemm``, ``fp8ds_gemm_batched``,
-``fp8ds_adamw``.
+``fp8ds_linear_batched``, ``fp8ds_adamw``.
 """
 
 from __future__ import annotations
@@ -89,6 +89,10 @@ def _declare(lib):
     lib.fp8ds_gemm_batched.restype = i32
     lib.fp8ds_gemm_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i32, i64, i64, vp, vp, i32,
                                        i64, i64, vp, vp, i32, i64, i64, vp, i32, vp]
+    lib.fp8ds_linear_batched.restype = i32
+    lib.fp8ds_linear_batched.argtypes = [i64, i64, i64, i64, i32, vp, i64, i32, vp, i64, i32, i32,
+                                         vp, vp, i32, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp,
+                                         i64, vp, vp]
     return lib
 
 
@@ -104,6 +108,43 @@ def lib():
                         "(the FP8 path has no CPU fallback)")
                 _lib = _declare(ctypes.CDLL(LIB_PATH))
     return _lib
+
+
+# While a launch sequence is being prepared (see `prepare`), the C calls are
+# validated by their wrappers and recorded here instead of made.
+_recording = threading.local()
+
+
+def _call(name: str, *args):
+    rec = getattr(_recording, "calls", None)
+    if rec is not None:
+        rec.append((getattr(lib(), name), args))
+        return
+    _check(getattr(lib(), name)(*args))
+
+
+def prepare(fn):
+    """Run ``fn()`` once with every library call it makes validated and recorded
+    instead of launched; return a function that launches the recorded calls, in
+    order, with the same arguments (the same tensors and stream) each time it is
+    called.  For tight loops whose Python-side checks would otherwise cost more
+    than the kernels: the step must not change Python-side state between calls
+    (``BatchedDelayedScalingLinear.step`` does not; ``DelayedScalingLinear.step``
+    alternates accumulator sets and must be called itself)."""
+    if getattr(_recording, "calls", None) is not None:
+        raise RuntimeError("prepare() does not nest")
+    _recording.calls = []
+    try:
+        fn()
+        calls = tuple(_recording.calls)
+    finally:
+        _recording.calls = None
+
+    def launch():
+        for f, args in calls:
+            _check(f(*args))
+
+    return launch
 
 
 def _check(status: int):
@@ -178,7 +219,7 @@ def fp8ds_amax(x, amax, stream=None):
 
     _need(x, "x", (torch.bfloat16, torch.float32), 0)
     _need(amax, "amax", (torch.float32,), 1)
-    _check(lib().fp8ds_amax(_ptr(x), _dtype_code(x), x.numel(), _ptr(amax), _stream(stream)))
+    _call("fp8ds_amax", _ptr(x), _dtype_code(x), x.numel(), _ptr(amax), _stream(stream))
 
 
 def fp8ds_cast(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_count=None,
@@ -195,9 +236,9 @@ def fp8ds_cast(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_count
     _need(scale_used, "scale_used", f32, 1)
     _need(amax, "amax", f32, 1)
     _need(sat_count, "sat_count", (torch.int64,), 1)
-    _check(lib().fp8ds_cast(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
-                            _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(sat_count),
-                            _stream(stream)))
+    _call("fp8ds_cast", _ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
+          _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(sat_count),
+          _stream(stream))
 
 
 def fp8ds_cast_acc(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_count=None,
@@ -214,9 +255,9 @@ def fp8ds_cast_acc(x, fmt, scale, q, q_t=None, scale_used=None, amax=None, sat_c
     _need(scale_used, "scale_used", f32, 1)
     _need(amax, "amax", f32, 1)
     _need(sat_count, "sat_count", (torch.int64,), 1)
-    _check(lib().fp8ds_cast_acc(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
-                                _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(sat_count),
-                                _stream(stream)))
+    _call("fp8ds_cast_acc", _ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
+          _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(sat_count),
+          _stream(stream))
 
 
 HEALTH_COUNTS = 5
@@ -241,9 +282,9 @@ def fp8ds_cast_health(x, fmt, scale, q, counts, q_t=None, scale_used=None, amax=
     if counts is None:
         raise ValueError("counts is required")
     _need(counts, "counts", (torch.int64,), HEALTH_COUNTS)
-    _check(lib().fp8ds_cast_health(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
-                                   _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(counts),
-                                   _stream(stream)))
+    _call("fp8ds_cast_health", _ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(scale), _ptr(q),
+          _ptr(q_t), _ptr(scale_used), _ptr(amax), _ptr(counts),
+          _stream(stream))
 
 
 def fp8ds_cast_batched(x, fmt, scale, q, scale_used=None, amax=None, sat_count=None, stream=None):
@@ -262,10 +303,10 @@ def fp8ds_cast_batched(x, fmt, scale, q, scale_used=None, amax=None, sat_count=N
     _need(scale_used, "scale_used", f32, batch)
     _need(amax, "amax", f32, batch)
     _need(sat_count, "sat_count", (torch.int64,), batch)
-    _check(lib().fp8ds_cast_batched(_ptr(x), _dtype_code(x), batch, n,
-                                    x.stride(0) if batch else n, fmt, _ptr(scale), _ptr(q),
-                                    q.stride(0) if batch else n, _ptr(scale_used), _ptr(amax),
-                                    _ptr(sat_count), _stream(stream)))
+    _call("fp8ds_cast_batched", _ptr(x), _dtype_code(x), batch, n,
+          x.stride(0) if batch else n, fmt, _ptr(scale), _ptr(q),
+          q.stride(0) if batch else n, _ptr(scale_used), _ptr(amax),
+          _ptr(sat_count), _stream(stream))
 
 
 def fp8ds_scale_update(history, cursor, amax, fmts, algo, margin, scale, scale_inv=None,
@@ -286,9 +327,9 @@ def fp8ds_scale_update(history, cursor, amax, fmts, algo, margin, scale, scale_i
     _need(scale, "scale", f32, n)
     _need(scale_inv, "scale_inv", f32, n)
     arr = (ctypes.c_int * n)(*[int(f) for f in fmts[:n]])
-    _check(lib().fp8ds_scale_update(n, L, _ptr(history), _ptr(cursor), _ptr(amax),
-                                    ctypes.cast(arr, ctypes.c_void_p), algo, margin, _ptr(scale),
-                                    _ptr(scale_inv), _stream(stream)))
+    _call("fp8ds_scale_update", n, L, _ptr(history), _ptr(cursor), _ptr(amax),
+          ctypes.cast(arr, ctypes.c_void_p), algo, margin, _ptr(scale),
+          _ptr(scale_inv), _stream(stream))
 
 
 def fp8ds_scale_update_clear(history, cursor, amax, fmts, algo, margin, scale, clear,
@@ -309,10 +350,10 @@ def fp8ds_scale_update_clear(history, cursor, amax, fmts, algo, margin, scale, c
     if not clear.is_cuda or not clear.is_contiguous():
         raise ValueError("clear: expected a contiguous CUDA tensor")
     arr = (ctypes.c_int * n)(*[int(f) for f in fmts[:n]])
-    _check(lib().fp8ds_scale_update_clear(n, L, _ptr(history), _ptr(cursor), _ptr(amax),
-                                          ctypes.cast(arr, ctypes.c_void_p), algo, margin,
-                                          _ptr(scale), _ptr(scale_inv), _ptr(clear),
-                                          clear.numel() * clear.element_size(), _stream(stream)))
+    _call("fp8ds_scale_update_clear", n, L, _ptr(history), _ptr(cursor), _ptr(amax),
+          ctypes.cast(arr, ctypes.c_void_p), algo, margin,
+          _ptr(scale), _ptr(scale_inv), _ptr(clear),
+          clear.numel() * clear.element_size(), _stream(stream))
 
 
 def _check_gemm(opa, opb, M, N, K, batch, a, lda, stride_a, scale_a, b, ldb, stride_b, scale_b, c,
@@ -342,18 +383,18 @@ def fp8ds_gemm(opa, opb, M, N, K, a, fa, lda, scale_a, b, fb, ldb, scale_b, c, l
                stream=None, mma=MMA_EXACT):
     """``c = dequant(op(a) @ op(b))`` with FP32 accumulation; ``c`` is bf16 or fp32."""
     _check_gemm(opa, opb, M, N, K, 1, a, lda, 0, scale_a, b, ldb, 0, scale_b, c, ldc, 0, amax_c)
-    _check(lib().fp8ds_gemm(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_a), _ptr(b), fb, ldb,
-                            _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c), mma,
-                            _stream(stream)))
+    _call("fp8ds_gemm", opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_a), _ptr(b), fb, ldb,
+          _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c), mma,
+          _stream(stream))
 
 
 def fp8ds_gemm_acc(opa, opb, M, N, K, a, fa, lda, scale_a, b, fb, ldb, scale_b, c, ldc,
                    amax_c=None, stream=None, mma=MMA_EXACT):
     """:func:`fp8ds_gemm` that max-accumulates the output amax into ``amax_c``."""
     _check_gemm(opa, opb, M, N, K, 1, a, lda, 0, scale_a, b, ldb, 0, scale_b, c, ldc, 0, amax_c)
-    _check(lib().fp8ds_gemm_acc(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_a), _ptr(b), fb,
-                                ldb, _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c),
-                                mma, _stream(stream)))
+    _call("fp8ds_gemm_acc", opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_a), _ptr(b), fb,
+          ldb, _ptr(scale_b), _ptr(c), _dtype_code(c), ldc, _ptr(amax_c),
+          mma, _stream(stream))
 
 
 def fp8ds_gemm_batched(opa, opb, M, N, K, batch, a, fa, lda, stride_a, scale_a, b, fb, ldb,
@@ -362,11 +403,47 @@ def fp8ds_gemm_batched(opa, opb, M, N, K, batch, a, fa, lda, stride_a, scale_a, 
     """``batch`` GEMMs of one shape with per-problem scales and output amax."""
     _check_gemm(opa, opb, M, N, K, batch, a, lda, stride_a, scale_a, b, ldb, stride_b, scale_b, c,
                 ldc, stride_c, amax_c)
-    _check(lib().fp8ds_gemm_batched(opa, opb, M, N, K, batch, _ptr(a), fa, lda, stride_a,
-                                    _ptr(scale_a), _ptr(b), fb, ldb, stride_b, _ptr(scale_b),
-                                    _ptr(c), _dtype_code(c), ldc, stride_c, _ptr(amax_c), mma,
-                                    _stream(stream)))
+    _call("fp8ds_gemm_batched", opa, opb, M, N, K, batch, _ptr(a), fa, lda, stride_a,
+          _ptr(scale_a), _ptr(b), fb, ldb, stride_b, _ptr(scale_b),
+          _ptr(c), _dtype_code(c), ldc, stride_c, _ptr(amax_c), mma,
+          _stream(stream))
 
+
+def fp8ds_linear_batched(x, w, fx, fw, history, cursor, algo, margin, scale, amax, y,
+                         scale_used=None, sat_count=None, xq=None, wq=None, amax_y=None,
+                         stream=None):
+    """Forward step of ``batch`` small Linears in one launch: ``x`` [B, M, K] and
+    ``w`` [B, K, N] (bf16, contiguous) are cast with their delayed scales
+    (``scale[i]`` for X_i, ``scale[B + i]`` for W_i; codes into ``xq``, ``wq``),
+    ``y`` [B, M, N] bf16 = the exact-datapath products, and the 2B tensors'
+    ``history`` [2B, L], ``cursor``, ``scale`` are updated with this step's
+    ``amax`` [2B]."""
+    import torch
+
+    B, M, K = x.shape
+    B2, K2, N = w.shape
+    if B2 != B or K2 != K:
+        raise ValueError(f"x {tuple(x.shape)} and w {tuple(w.shape)} do not match")
+    n, L = history.shape
+    if n != 2 * B:
+        raise ValueError(f"history: {n} tensors for a batch of {B}")
+    bf, f32 = (torch.bfloat16,), (torch.float32,)
+    _need(x, "x", bf, B * M * K)
+    _need(w, "w", bf, B * K * N)
+    _need(y, "y", bf, B * M * N)
+    _need(xq, "xq", (torch.uint8,), B * M * K)
+    _need(wq, "wq", (torch.uint8,), B * K * N)
+    _need(history, "history", f32, n * L)
+    _need(cursor, "cursor", (torch.int32,), n)
+    for t, name in ((scale, "scale"), (amax, "amax"), (scale_used, "scale_used")):
+        _need(t, name, f32, n)
+    _need(sat_count, "sat_count", (torch.int64,), n)
+    _need(amax_y, "amax_y", f32, B)
+    _call("fp8ds_linear_batched", B, M, N, K, BF16, _ptr(x), M * K, fx, _ptr(w), K * N, fw, L,
+          _ptr(history), _ptr(cursor), algo, margin, _ptr(scale),
+          _ptr(scale_used), _ptr(amax), _ptr(sat_count), _ptr(xq),
+          M * K, _ptr(wq), K * N, _ptr(y), M * N, _ptr(amax_y),
+          _stream(stream))
 
 
 def fp8ds_adamw(w, g, m, v, lr, beta1, beta2, eps, weight_decay, step, grad_scale=1.0,
@@ -397,11 +474,11 @@ def fp8ds_adamw(w, g, m, v, lr, beta1, beta2, eps, weight_decay, step, grad_scal
     _need(scale_used, "scale_used", f32, 1)
     _need(amax, "amax", f32, 1)
     _need(sat_count, "sat_count", (torch.int64,), 1)
-    _check(lib().fp8ds_adamw(_ptr(w), _ptr(g), _dtype_code(g), _ptr(m), _ptr(v), rows, cols,
-                             float(lr), float(beta1), float(beta2), float(eps),
-                             float(weight_decay), float(grad_scale), int(step), _ptr(grad_amax),
-                             fmt, _ptr(scale), _ptr(q), _ptr(q_t), _ptr(scale_used), _ptr(amax),
-                             _ptr(sat_count), _stream(stream)))
+    _call("fp8ds_adamw", _ptr(w), _ptr(g), _dtype_code(g), _ptr(m), _ptr(v), rows, cols,
+          float(lr), float(beta1), float(beta2), float(eps),
+          float(weight_decay), float(grad_scale), int(step), _ptr(grad_amax),
+          fmt, _ptr(scale), _ptr(q), _ptr(q_t), _ptr(scale_used), _ptr(amax),
+          _ptr(sat_count), _stream(stream))
 
 
 
@@ -421,8 +498,8 @@ def fp8ds_cast_rowwise(x, fmt, margin, q, scale, scale_inv=None, amax=None, stre
     _need(scale, "scale", f32, rows)
     _need(scale_inv, "scale_inv", f32, rows)
     _need(amax, "amax", f32, rows)
-    _check(lib().fp8ds_cast_rowwise(_ptr(x), _dtype_code(x), rows, cols, fmt, int(margin), _ptr(q),
-                                    _ptr(scale), _ptr(scale_inv), _ptr(amax), _stream(stream)))
+    _call("fp8ds_cast_rowwise", _ptr(x), _dtype_code(x), rows, cols, fmt, int(margin), _ptr(q),
+          _ptr(scale), _ptr(scale_inv), _ptr(amax), _stream(stream))
 
 
 def fp8ds_cast_current(x, fmt, margin, q, scale, amax, q_t=None, scale_inv=None, sat_count=None,
@@ -441,9 +518,9 @@ def fp8ds_cast_current(x, fmt, margin, q, scale, amax, q_t=None, scale_inv=None,
     _need(amax, "amax", f32, 1)
     _need(scale_inv, "scale_inv", f32, 1)
     _need(sat_count, "sat_count", (torch.int64,), 1)
-    _check(lib().fp8ds_cast_current(_ptr(x), _dtype_code(x), rows, cols, fmt, int(margin), _ptr(q),
-                                    _ptr(q_t), _ptr(scale), _ptr(scale_inv), _ptr(amax),
-                                    _ptr(sat_count), _stream(stream)))
+    _call("fp8ds_cast_current", _ptr(x), _dtype_code(x), rows, cols, fmt, int(margin), _ptr(q),
+          _ptr(q_t), _ptr(scale), _ptr(scale_inv), _ptr(amax),
+          _ptr(sat_count), _stream(stream))
 
 
 def fp8ds_gemm_rowcol(opa, opb, M, N, K, a, fa, lda, scale_inv_a, b, fb, ldb, scale_inv_b, c, ldc,
@@ -455,9 +532,9 @@ def fp8ds_gemm_rowcol(opa, opb, M, N, K, a, fa, lda, scale_inv_a, b, fb, ldb, sc
     _check_gemm(opa, opb, M, N, K, 1, a, lda, 0, None, b, ldb, 0, None, c, ldc, 0, amax_c)
     _need(scale_inv_a, "scale_inv_a", (torch.float32,), M)
     _need(scale_inv_b, "scale_inv_b", (torch.float32,), N)
-    _check(lib().fp8ds_gemm_rowcol(opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_inv_a), _ptr(b),
-                                   fb, ldb, _ptr(scale_inv_b), _ptr(c), _dtype_code(c), ldc,
-                                   _ptr(amax_c), _stream(stream)))
+    _call("fp8ds_gemm_rowcol", opa, opb, M, N, K, _ptr(a), fa, lda, _ptr(scale_inv_a), _ptr(b),
+          fb, ldb, _ptr(scale_inv_b), _ptr(c), _dtype_code(c), ldc,
+          _ptr(amax_c), _stream(stream))
 
 
 def fp8ds_cast_mx(x, fmt, q, scales, q_t=None, scales_t=None, stream=None):
@@ -476,8 +553,8 @@ def fp8ds_cast_mx(x, fmt, q, scales, q_t=None, scales_t=None, stream=None):
     _need(scales, "scales", (torch.uint8,), rows * cols // 32)
     _need(q_t, "q_t", (torch.uint8,), rows * cols)
     _need(scales_t, "scales_t", (torch.uint8,), rows * cols // 32)
-    _check(lib().fp8ds_cast_mx(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(q), _ptr(scales),
-                               _ptr(q_t), _ptr(scales_t), _stream(stream)))
+    _call("fp8ds_cast_mx", _ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(q), _ptr(scales),
+          _ptr(q_t), _ptr(scales_t), _stream(stream))
 
 
 def fp8ds_gemm_mx(M, N, K, a, fa, lda, scales_a, ld_scales_a, b, fb, ldb, scales_b, ld_scales_b,
@@ -492,9 +569,9 @@ def fp8ds_gemm_mx(M, N, K, a, fa, lda, scales_a, ld_scales_a, b, fb, ldb, scales
         _need(t, name, (torch.uint8,), n, contiguous=False)
     _need(c, "c", (torch.bfloat16, torch.float32), _span(M, N, ldc), contiguous=False)
     _need(amax_c, "amax_c", (torch.float32,), 1)
-    _check(lib().fp8ds_gemm_mx(M, N, K, _ptr(a), fa, lda, _ptr(scales_a), ld_scales_a, _ptr(b), fb,
-                               ldb, _ptr(scales_b), ld_scales_b, _ptr(c), _dtype_code(c), ldc,
-                               _ptr(amax_c), mma, _stream(stream)))
+    _call("fp8ds_gemm_mx", M, N, K, _ptr(a), fa, lda, _ptr(scales_a), ld_scales_a, _ptr(b), fb,
+          ldb, _ptr(scales_b), ld_scales_b, _ptr(c), _dtype_code(c), ldc,
+          _ptr(amax_c), mma, _stream(stream))
 
 
 def abi_version() -> int:

@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfp8ds.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["api.cpp", "cast.hip", "adamw.hip", "finer.hip", "mx.hip", "gemm_mx.hip", "gemm_rowcol.hip", "scale_update.hip", "gemm_exact.hip", "gemm_fp8.hip"]
+SOURCES = ["api.cpp", "cast.hip", "adamw.hip", "finer.hip", "mx.hip", "gemm_mx.hip", "gemm_rowcol.hip", "scale_update.hip", "gemm_exact.hip", "gemm_fp8.hip", "linear_batched.hip"]
 
 ARCH = os.environ.get("FP8DS_OFFLOAD_ARCH", "gfx950")
 

@@ -339,6 +339,67 @@ int fp8ds_gemm_batched(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t
                      B, fb, ldb, stride_b, scale_b, C, ct, ldc, stride_c, amax_c, mma, stream);
 }
 
+int fp8ds_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, fp8ds_dtype xt,
+                         const void* x, int64_t stride_x, fp8ds_format fx, const void* w,
+                         int64_t stride_w, fp8ds_format fw, int hist_len, float* history,
+                         int32_t* cursor, fp8ds_algo algo, int margin, float* scale,
+                         float* scale_used, float* amax, uint64_t* sat_count, uint8_t* xq,
+                         int64_t stride_xq, uint8_t* wq, int64_t stride_wq, void* y,
+                         int64_t stride_y, float* amax_y, hipStream_t stream) {
+  const char* who = "fp8ds_linear_batched";
+  if (!valid_dtype(xt)) return fail(FP8DS_ERR_ENUM, "%s: bad dtype %d", who, (int)xt);
+  if (xt != FP8DS_BF16) return fail(FP8DS_ERR_UNSUPPORTED, "%s: only BF16 inputs", who);
+  if (!valid_fmt(fx) || !valid_fmt(fw)) return fail(FP8DS_ERR_ENUM, "%s: bad format", who);
+  if (algo != FP8DS_ALGO_MAX && algo != FP8DS_ALGO_MOST_RECENT)
+    return fail(FP8DS_ERR_ENUM, "%s: bad algo %d", who, (int)algo);
+  if (batch < 1 || batch > 65535)
+    return fail(FP8DS_ERR_SHAPE, "%s: batch %lld not in [1, 65535]", who, (long long)batch);
+  auto dim_ok = [](int64_t v) { return v >= 16 && v <= 256 && v % 16 == 0; };
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K))
+    return fail(FP8DS_ERR_SHAPE, "%s: M, N, K (%lld, %lld, %lld) must be multiples of 16 in "
+                "[16, 256]", who, (long long)M, (long long)N, (long long)K);
+  if (hist_len < 1 || hist_len > 65536)
+    return fail(FP8DS_ERR_SHAPE, "%s: hist_len %d not in [1, 65536]", who, hist_len);
+  if (margin < -126 || margin > 126)
+    return fail(FP8DS_ERR_SHAPE, "%s: margin %d not in [-126, 126]", who, margin);
+  if (!x || !w || !history || !cursor || !scale || !amax || !y)
+    return fail(FP8DS_ERR_NULL, "%s: x, w, history, cursor, scale, amax and y are required", who);
+  if (stride_x < M * K || stride_w < K * N || stride_y < M * N || (xq && stride_xq < M * K) ||
+      (wq && stride_wq < K * N) || stride_x > kMaxElems || stride_w > kMaxElems ||
+      stride_y > kMaxElems || stride_xq > kMaxElems || stride_wq > kMaxElems)
+    return fail(FP8DS_ERR_SHAPE, "%s: every stride must be at least its problem's size", who);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (xq && !aligned16(xq)) ||
+      (wq && !aligned16(wq)) || (stride_x * 2) % 16 || (stride_w * 2) % 16 ||
+      (stride_y * 2) % 16 || (xq && stride_xq % 16) || (wq && stride_wq % 16))
+    return fail(FP8DS_ERR_ALIGN, "%s: pointers and strides must keep 16-byte alignment", who);
+  fp8ds::LinearBatchedArgs a;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.batch = (int)batch;
+  a.x = static_cast<const uint16_t*>(x);
+  a.stride_x = stride_x;
+  a.w = static_cast<const uint16_t*>(w);
+  a.stride_w = stride_w;
+  a.xq = xq;
+  a.stride_xq = xq ? stride_xq : 0;
+  a.wq = wq;
+  a.stride_wq = wq ? stride_wq : 0;
+  a.y = static_cast<uint16_t*>(y);
+  a.stride_y = stride_y;
+  a.amax_y = amax_y;
+  a.history = history;
+  a.cursor = cursor;
+  a.hist_len = hist_len;
+  a.algo = (int)algo;
+  a.margin = margin;
+  a.scale = scale;
+  a.scale_used = scale_used;
+  a.amax = amax;
+  a.sat = reinterpret_cast<unsigned long long*>(sat_count);
+  return hip_status(fp8ds::launch_linear_batched(a, (int)fx, (int)fw, stream), who);
+}
+
 int fp8ds_adamw(float* w, const void* g, fp8ds_dtype gt, float* m, float* v, int64_t rows,
                 int64_t cols, float lr, float beta1, float beta2, float eps, float weight_decay,
                 float grad_scale, int64_t step, const float* grad_amax, fp8ds_format fmt,

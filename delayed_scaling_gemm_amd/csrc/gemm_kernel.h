@@ -502,8 +502,10 @@ __device__ __forceinline__ float dq(float a, float r, float c) {
 // `stage0`, `stage1`: the two halves of the operand tiles' LDS (at least NW/2 WTM
 // WTN 2 bytes each), free once every wave has passed the epilogue's first
 // barrier; the first NW/2 waves stage their blocks in `stage0`, the others in
-// `stage1`.  `red` holds NW words.
-template <int BM, int BN, int FM, int FN, int WTM, int WTN, bool VS = false, int NW = 4>
+// `stage1`.  `red` holds NW words.  AMAX_STORE: the workgroup is the only one of
+// its output, and stores the output amax instead of combining it atomically.
+template <int BM, int BN, int FM, int FN, int WTM, int WTN, bool VS = false, int NW = 4,
+          bool AMAX_STORE = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM][FN], int64_t m0,
                                          int64_t n0, int wm, int wn, int tid, int64_t bz, float d,
                                          uint32_t* red, uint8_t* stage0, uint8_t* stage1) {
@@ -639,7 +641,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
       uint32_t m = red[0];
 #pragma unroll
       for (int w = 1; w < NW; ++w) m = max(m, red[w]);
-      atomicMax(p.amax_c + bz, canonical_amax_bits(m));
+      if constexpr (AMAX_STORE) p.amax_c[bz] = canonical_amax_bits(m);
+      else atomicMax(p.amax_c + bz, canonical_amax_bits(m));
     }
   }
 }

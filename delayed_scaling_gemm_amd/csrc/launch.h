@@ -86,6 +86,35 @@ hipError_t launch_scale_update(int n, int hist_len, float* history, int32_t* cur
                                float* scale, float* scale_inv, hipStream_t stream,
                                uint32_t* clear = nullptr, int64_t n_clear = 0);
 
+// Forward step of `batch` small Linears in one launch, one workgroup per problem:
+// casts of X_i and W_i with their delayed scales, Y_i = X_i W_i on the exact
+// datapath with the dequant epilogue, and the scaling-state update of both
+// tensors.  BF16 inputs; M, N, K multiples of 16 in [16, 256]; every pointer
+// 16-byte aligned and every stride a multiple of 16 bytes.  Tensor t of the
+// per-tensor arrays ([2 batch]) is X_t for t < batch, W_{t - batch} after.
+struct LinearBatchedArgs {
+  int M, N, K, batch;
+  const uint16_t* x;     // [batch][M][K]
+  int64_t stride_x;      // elements
+  const uint16_t* w;     // [batch][K][N]
+  int64_t stride_w;
+  uint8_t* xq;           // [batch][M][K] or null
+  int64_t stride_xq;     // bytes
+  uint8_t* wq;           // [batch][K][N] or null
+  int64_t stride_wq;
+  uint16_t* y;           // [batch][M][N] BF16
+  int64_t stride_y;      // elements
+  float* amax_y;         // [batch] or null
+  float* history;        // [2 batch][hist_len]
+  int32_t* cursor;       // [2 batch]
+  int hist_len, algo, margin;
+  float* scale;          // [2 batch] in: this step's scales; out: the next step's
+  float* scale_used;     // [2 batch] or null: this step's scales
+  float* amax;           // [2 batch]: this step's amax of each input
+  unsigned long long* sat;  // [2 batch] or null: saturated values of each cast
+};
+hipError_t launch_linear_batched(const LinearBatchedArgs& a, int fx, int fw, hipStream_t stream);
+
 // FP8 GEMM.  opa/opb: 0 = N, 1 = T.  out_bf16: BF16 output, else FP32.
 struct GemmProblem {
   int opa, opb;

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FP8DS_ABI_VERSION 7
+#define FP8DS_ABI_VERSION 8
 
 typedef enum {
   FP8DS_OK = 0,
@@ -302,6 +302,50 @@ int fp8ds_gemm_batched(fp8ds_op opa, fp8ds_op opb, int64_t M, int64_t N, int64_t
                        int64_t stride_b, const float* scale_b, void* C, fp8ds_dtype ct,
                        int64_t ldc, int64_t stride_c, float* amax_c, fp8ds_mma mma,
                        hipStream_t stream);
+
+/*
+ * fp8ds_linear_batched -- the whole forward step of `batch` independent small
+ * Linears Y_i = X_i W_i, each with its own delayed scaling of X_i and W_i, in one
+ * launch.  [P3] §适用场景 (many small matrices among the cases to treat with care)
+ * and §常见误区 误区一 (with small matrices the conversion work can cancel the
+ * FP8 gain): one workgroup per problem reads X_i and W_i once, casts them, keeps
+ * the codes on chip for the product and updates both tensors' scaling state, so
+ * the codes are never read back and no other launch is needed.
+ *
+ * Per problem i (tensor t = i is X_i, tensor t = batch + i is W_i):
+ *   xq_i = cast(X_i, scale[i]), wq_i = cast(W_i, scale[batch + i])   (fp8ds_cast)
+ *   y_i  = fp8ds_gemm(N, N) of xq_i and wq_i with those scales, BF16, amax_y[i]
+ *   then for both tensors, with this step's amax: fp8ds_scale_update
+ * The results equal those of fp8ds_cast_batched (X, then W), fp8ds_gemm_batched
+ * (exact datapath) and fp8ds_scale_update over the 2 * batch tensors, in that
+ * order; the outputs amax, sat_count, amax_y are stored, not combined into.
+ *
+ *   batch            1 .. 65535 problems
+ *   M, N, K          multiples of 16 in [16, 256]
+ *   x                [batch][M][K] BF16 (problem i at x + i*stride_x elements)
+ *   w                [batch][K][N] BF16 (at w + i*stride_w elements)
+ *   fx, fw           formats of the X and W codes
+ *   hist_len, history, cursor, algo, margin: as fp8ds_scale_update, over the
+ *                    2 * batch tensors ([2 batch][hist_len], [2 batch])
+ *   scale            [2 batch] in: this step's scales; out: the next step's
+ *   scale_used       [2 batch] (nullable): this step's scales
+ *   amax             [2 batch] out: max |X_i|, then max |W_i| (NaN canonical)
+ *   sat_count        [2 batch] (nullable) out: saturated values of each cast
+ *   xq, wq           (nullable) codes: [batch][M][K] at stride_xq bytes,
+ *                    [batch][K][N] at stride_wq bytes
+ *   y                [batch][M][N] BF16 at stride_y elements
+ *   amax_y           [batch] (nullable) out: max |y_i|
+ * Every pointer 16-byte aligned, every stride a multiple of 16 bytes, strides at
+ * least the problem's size.  Only the BF16 input dtype is supported
+ * (FP8DS_ERR_UNSUPPORTED otherwise); the products run on the exact datapath.
+ */
+int fp8ds_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, fp8ds_dtype xt,
+                         const void* x, int64_t stride_x, fp8ds_format fx, const void* w,
+                         int64_t stride_w, fp8ds_format fw, int hist_len, float* history,
+                         int32_t* cursor, fp8ds_algo algo, int margin, float* scale,
+                         float* scale_used, float* amax, uint64_t* sat_count, uint8_t* xq,
+                         int64_t stride_xq, uint8_t* wq, int64_t stride_wq, void* y,
+                         int64_t stride_y, float* amax_y, hipStream_t stream);
 
 /*
  * fp8ds_adamw -- fused AdamW step on FP32 master weights that also writes the

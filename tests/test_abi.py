@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
               "fp8ds_gemm", "fp8ds_gemm_batched", "fp8ds_status_string", "fp8ds_last_error",
               "fp8ds_abi_version", "fp8ds_adamw", "fp8ds_cast_health", "fp8ds_cast_rowwise",
               "fp8ds_cast_current", "fp8ds_gemm_rowcol", "fp8ds_cast_mx", "fp8ds_gemm_mx",
-              "fp8ds_cast_acc", "fp8ds_gemm_acc", "fp8ds_scale_update_clear"):
+              "fp8ds_cast_acc", "fp8ds_gemm_acc", "fp8ds_scale_update_clear",
+              "fp8ds_linear_batched"):
         assert n in names
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(dsg.LIB_PATH)
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert dsg.abi_version() == 7
+    assert dsg.abi_version() == 8
 
 
 def test_status_strings():
@@ -198,3 +199,38 @@ def test_accumulating_variants_validate_like_the_plain_calls():
     assert clr(2, 16, p, p, p, fmp, 0, 0, p, None, p + 0x102, 8, None) == -4   # misaligned
     assert clr(2, 16, p, p, p, fmp, 0, 0, p, None, p + 4, 8, None) == -7       # overlaps amax
     assert clr(0, 16, p, p, p, fmp, 0, 0, p, None, p + 0x100, 8, None) == -2   # as scale_update
+
+
+def test_linear_batched_validation_errors_without_gpu():
+    """fp8ds_linear_batched rejects bad sizes, enums, null pointers, short strides
+    and misalignment before any launch (CPU only)."""
+    L = dsg.lib()
+    p = 0x1000
+
+    def call(B=2, M=64, N=64, K=64, xt=1, x=p, sx=None, fx=0, w=p, sw=None, fw=0, L_=16,
+             hist=p, cur=p, algo=0, margin=0, scale=p, su=None, amax=p, sat=None, xq=None,
+             sxq=None, wq=None, swq=None, y=p, sy=None, amy=None):
+        sx = M * K if sx is None else sx
+        sw = K * N if sw is None else sw
+        sy = M * N if sy is None else sy
+        sxq = M * K if sxq is None else sxq
+        swq = K * N if swq is None else swq
+        st = L.fp8ds_linear_batched(B, M, N, K, xt, x, sx, fx, w, sw, fw, L_, hist, cur, algo,
+                                    margin, scale, su, amax, sat, xq, sxq, wq, swq, y, sy, amy,
+                                    None)
+        return st, L.fp8ds_last_error().decode()
+
+    assert call(xt=0)[0] == -6                      # FP32 inputs: not supported
+    assert call(xt=3)[0] == -3
+    assert call(fx=2)[0] == -3 and call(fw=-1)[0] == -3
+    assert call(algo=2)[0] == -3
+    for bad in (dict(B=0), dict(B=65536), dict(M=8), dict(N=272), dict(K=40), dict(L_=0),
+                dict(margin=127), dict(sx=64 * 64 - 16), dict(sy=16), dict(xq=p, sxq=16)):
+        st, msg = call(**bad)
+        assert st == -2 and "fp8ds_linear_batched" in msg, bad
+    for bad in (dict(x=None), dict(w=None), dict(hist=None), dict(cur=None), dict(scale=None),
+                dict(amax=None), dict(y=None)):
+        assert call(**bad)[0] == -1, bad
+    for bad in (dict(x=p + 8), dict(y=p + 2), dict(xq=p + 4), dict(sx=64 * 64 + 4),
+                dict(wq=p, swq=64 * 64 + 8)):
+        assert call(**bad)[0] == -4, bad
