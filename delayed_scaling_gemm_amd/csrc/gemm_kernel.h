@@ -647,6 +647,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
   }
 }
 
+// The number of workgroup barriers `epilogue` executes (for waves that do not
+// run it but must meet its barriers): two around the staging of full BF16 tiles,
+// one for the output amax.
+template <int BM, int BN>
+__device__ __forceinline__ int epilogue_barriers(const GemmArgs& p, int64_t m0, int64_t n0) {
+  const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+  return (!p.out_f32 && full ? 2 : 0) + (p.amax_c ? 1 : 0);
+}
+
 // ------------------------------------------------------------------ the kernel
 //
 // Both datapaths stage FP8 tiles of 128 K values per LDS row.  Lane l works on
@@ -666,20 +675,31 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const v16f (&acc)[FM
 //     under step 7.
 // FP8: a stage is 2 MFMA steps of K = 64 (32x32x64 F8F6F4), each on two chunks.
 
+// KS = 2: two groups of four waves share each output tile, group g taking the
+// g-th half of the K stages with LDS buffers of its own; at the end group 1
+// hands its partial sums to group 0 through LDS, which adds them to its own
+// (first half + second half, always in that order) and runs the epilogue.  For
+// grids of 128 x 128 tiles that give each CU one tile or less: twice the waves
+// per CU, without partial results in memory.
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT,
-          bool VS = false, bool MX = false>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
+          bool VS = false, bool MX = false, int KS = 1>
+__global__ __launch_bounds__(256 * KS, 1) void gemm_kernel(GemmArgs p) {
   static_assert(!MX || (DIRECT && A_KC && B_KC && !VS),
                 "MX blocks run along K: both operands K-contiguous, direct loads");
-  constexpr int NT = 256;
+  static_assert(KS == 1 || (KS == 2 && DIRECT && !MX && BM == 128 && BN == 128),
+                "the K split runs on direct loads of 128 x 128 tiles");
+  constexpr int NT = 256;  // threads per group
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int KB = 128;  // K values per stage
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a_g[KS][2][BM * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b_g[KS][2][BN * kRowBytes];
   __shared__ uint32_t red[4];
 
-  const int tid = threadIdx.x;
+  const int grp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);
+  uint8_t (*lds_a)[BM * kRowBytes] = lds_a_g[grp];
+  uint8_t (*lds_b)[BN * kRowBytes] = lds_b_g[grp];
+  const int tid = threadIdx.x & (NT - 1);  // thread within the group
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave >> 1, wn = wave & 1;
@@ -703,7 +723,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = (int)((K + KB - 1) / KB);
+  // stages of this group: [kbase, kbase + nk) (KS = 2 requires an even stage count)
+  const int nk = (int)((K + KB - 1) / KB) / KS;
+  const int kbase = grp * nk;
   // dequant factor (VS: the per-row / per-column factors are applied in the epilogue)
   const float d = (VS || MX) ? 1.0f : __fdiv_rn(1.0f, p.scale_a[bz] * p.scale_b[bz]);
   const int fr = lane & 31;
@@ -758,8 +780,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       const int la = lo, ha = hi < kIssuesA ? hi : kIssuesA;
       const int lb = lo > kIssuesA ? lo - kIssuesA : 0;
       const int hb = hi < kIssuesA + kIssuesB ? hi - kIssuesA : kIssuesB;
-      dla.issue((int64_t)kt * KB, lds_a[buf], la, ha);
-      dlb.issue((int64_t)kt * KB, lds_b[buf], lb, hb);
+      dla.issue((int64_t)(kt + kbase) * KB, lds_a[buf], la, ha);
+      dlb.issue((int64_t)(kt + kbase) * KB, lds_b[buf], lb, hb);
     }
   };
   if constexpr (EXACT) {
@@ -1098,6 +1120,41 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     if (nk > 0) stage(nk - 1, std::false_type{}, std::false_type{});
   }
 
+  if constexpr (KS == 2) {
+    // Group 1's partial sums through its own LDS (each wave's 16 KiB: float4 q
+    // of block (i, j) of lane l at ((i FN + j) 4 + q) 64 + l), added by the wave
+    // of group 0 with the same index.
+    static_assert(FM * FN * 16 * 64 * 4 * 2 == 2 * BM * kRowBytes, "two waves' sums per buffer");
+    f32x4_t* xch = reinterpret_cast<f32x4_t*>(wave < 2 ? &lds_a_g[1][0][0] : &lds_b_g[1][0][0]) +
+                   (wave & 1) * (FM * FN * 4 * 64);
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            xch[((i * FN + j) * 4 + q) * 64 + lane] =
+                f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
+    __syncthreads();
+    if (grp == 1) {
+      // the epilogue's barriers, which group 0 reaches there
+      const int nb = epilogue_barriers<BM, BN>(p, m0, n0);
+      for (int b = 0; b < nb; ++b) __syncthreads();
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t o = xch[((i * FN + j) * 4 + q) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = acc[i][j][4 * q + e] + o[e];
+        }
+  }
   epilogue<BM, BN, FM, FN, WTM, WTN, VS>(p, acc, m0, n0, wm, wn, tid, bz, d, red,
                                         reinterpret_cast<uint8_t*>(lds_a),
                                         reinterpret_cast<uint8_t*>(lds_b));
@@ -1106,7 +1163,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 // ------------------------------------------------------------------ dispatch
 
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool DIRECT, bool VS,
-          bool MX = false>
+          bool MX = false, int KS = 1>
 static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   GemmArgs a;
   a.M = q.M; a.N = q.N; a.K = q.K;
@@ -1122,15 +1179,17 @@ static hipError_t launch_cfg(const GemmProblem& q, hipStream_t stream) {
   a.sc_a = q.sc_a; a.sc_b = q.sc_b;
   a.ldsa = q.ldsa; a.ldsb = q.ldsb;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)q.batch);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, EXACT, DIRECT, VS, MX>), grid,
-                     dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_KC, B_KC, FA, FB, EXACT, DIRECT, VS, MX, KS>), grid,
+                     dim3(256 * KS), 0, stream, a);
   return hipGetLastError();
 }
 
 // K a multiple of the stage depth and operands in aligned 16-byte chunks: LDS is
 // filled by direct loads; otherwise through registers.
+// ks2: run 128 x 128 tiles as two K halves per workgroup (K a multiple of 256,
+// direct loads only).
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, bool EXACT, bool VS>
-static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream) {
+static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream, bool ks2 = false) {
   {
     // Direct loads move aligned 16-byte chunks; MN-contiguous operands are
     // loaded in whole chunks along M / N.
@@ -1146,43 +1205,54 @@ static hipError_t launch_direct(const GemmProblem& q, hipStream_t stream) {
                       (A_KC ? fits(q.M, q.K, q.lda) : fits(q.K, q.M, q.lda));
     const bool b_ok = aligned(q.B, q.ldb, q.stride_b) && (B_KC || q.N % 16 == 0) &&
                       (B_KC ? fits(q.N, q.K, q.ldb) : fits(q.K, q.N, q.ldb));
-    if (q.K % 128 == 0 && a_ok && b_ok)
+    if (q.K % 128 == 0 && a_ok && b_ok) {
+      if constexpr (BM == 128 && BN == 128) {
+        if (ks2 && q.K % 256 == 0)
+          return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, true, VS, false, 2>(q, stream);
+      }
       return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, true, VS>(q, stream);
+    }
   }
   return launch_cfg<BM, BN, A_KC, B_KC, FA, FB, EXACT, false, VS>(q, stream);
 }
 
 template <int BM, int BN, bool A_KC, bool B_KC, bool EXACT, bool VS>
-static hipError_t launch_layout(const GemmProblem& q, hipStream_t s) {
-  if (q.fa == kE4M3 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE4M3, EXACT, VS>(q, s);
-  if (q.fa == kE4M3 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE5M2, EXACT, VS>(q, s);
-  if (q.fa == kE5M2 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE4M3, EXACT, VS>(q, s);
-  if (q.fa == kE5M2 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE5M2, EXACT, VS>(q, s);
+static hipError_t launch_layout(const GemmProblem& q, hipStream_t s, bool ks2) {
+  if (q.fa == kE4M3 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE4M3, EXACT, VS>(q, s, ks2);
+  if (q.fa == kE4M3 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE4M3, kE5M2, EXACT, VS>(q, s, ks2);
+  if (q.fa == kE5M2 && q.fb == kE4M3) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE4M3, EXACT, VS>(q, s, ks2);
+  if (q.fa == kE5M2 && q.fb == kE5M2) return launch_direct<BM, BN, A_KC, B_KC, kE5M2, kE5M2, EXACT, VS>(q, s, ks2);
   return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, bool EXACT, bool VS>
-static hipError_t launch_tile(const GemmProblem& q, hipStream_t s) {
-  if (q.opa == 0 && q.opb == 0) return launch_layout<BM, BN, true, false, EXACT, VS>(q, s);  // NN
-  if (q.opa == 0 && q.opb == 1) return launch_layout<BM, BN, true, true, EXACT, VS>(q, s);   // NT
-  if (q.opa == 1 && q.opb == 0) return launch_layout<BM, BN, false, false, EXACT, VS>(q, s); // TN
+static hipError_t launch_tile(const GemmProblem& q, hipStream_t s, bool ks2 = false) {
+  if (q.opa == 0 && q.opb == 0) return launch_layout<BM, BN, true, false, EXACT, VS>(q, s, ks2);  // NN
+  if (q.opa == 0 && q.opb == 1) return launch_layout<BM, BN, true, true, EXACT, VS>(q, s, ks2);   // NT
+  if (q.opa == 1 && q.opb == 0) return launch_layout<BM, BN, false, false, EXACT, VS>(q, s, ks2); // TN
   return hipErrorInvalidValue;
 }
 
 // Tile choice: 256 x 256 tiles when they alone give every CU at least one tile
 // and K is long enough to amortise their longer prologue and epilogue, else
-// 128 x 128 tiles (two resident per CU).  Measured on MI355X: with K <= 2048
-// the smaller tiles are 9-22% faster (512 x 256^3 batched: 52 -> 46 us;
-// 16384 x 4096 x 2048: 267 -> 243 us), from K = 4096 on the larger ones are
-// 3-10% faster.
-constexpr int64_t kBigTileMinK = 4096;
+// 128 x 128 tiles (two resident per CU).  Measured on MI355X: from K = 2048 on
+// the larger tiles are 10-17% faster (16384 x 4096 x 2048 NT: 226 -> 205 us;
+// 8192 x 4096 x 2048 NN: 125 -> 106 us); at K = 1024 the two are within noise
+// of each other, and below that the smaller ones are faster (512 x 256^3
+// batched: 52 -> 46 us).
+constexpr int64_t kBigTileMinK = 2048;
+// 128 x 128 tiles with at most one per CU (e.g. a 4096 x 1024 weight gradient)
+// run as two K halves per workgroup once K is this long.
+constexpr int64_t kSplitMinK = 1024;
 
 template <bool EXACT, bool VS = false>
 static hipError_t launch_path(const GemmProblem& q, int num_cus, hipStream_t stream) {
   if (q.M <= 0 || q.N <= 0 || q.batch <= 0) return hipSuccess;
   const int64_t big_tiles = ((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
   if (big_tiles >= num_cus && q.K >= kBigTileMinK) return launch_tile<256, 256, EXACT, VS>(q, stream);
-  return launch_tile<128, 128, EXACT, VS>(q, stream);
+  const int64_t tiles = ((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
+  const bool ks2 = tiles <= num_cus && q.K >= kSplitMinK;
+  return launch_tile<128, 128, EXACT, VS>(q, stream, ks2);
 }
 
 }  // namespace fp8ds
