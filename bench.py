@@ -576,11 +576,12 @@ def main():
         lin.step(x, w, dy)  # also allocates the output buffers
     torch.cuda.synchronize()
 
-    # Per-kernel durations (the roofline figures), before the timed region: each
-    # launch of the step K times back to back between two events on the library's
-    # stream, the inputs rotated over the input sets (events between launches
-    # would add several microseconds to every interval).  The scaling state is
-    # restored afterwards.
+    # Per-kernel durations, before the timed region: each launch of the step K
+    # times back to back between two events on the library's stream, the inputs
+    # rotated over the input sets (events between launches would add several
+    # microseconds to every interval).  These are the casts' and the scale
+    # update's figures; the GEMMs' (the roofline) are taken again inside the step
+    # below.  The scaling state is restored afterwards.
     print(f"[bench] per-kernel timing, {args.steps} launches each", file=sys.stderr, flush=True)
     saved = [t.clone() for t in (lin.history, lin.cursor, lin.scale, lin._acc)]
     per = {}
@@ -596,6 +597,30 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         per[name] = e0.elapsed_time(e1) / args.steps
+    # The GEMMs again, in the step: K full steps of the launches with events
+    # around the one GEMM being timed.  Back to back, the same GEMM runs several
+    # percent longer than between the step's memory-bound casts (measured in the
+    # kernel trace: ~410 against ~390 us for the dX GEMM; the matrix cores alone
+    # draw more power), so these are the figures of the step; each interval also
+    # holds the event pair's own ~1-2 us.
+    per_b2b = {}
+    for name in ("gemm_fwd_nt", "gemm_dgrad_nt", "gemm_wgrad_tn"):
+        j = names.index(name)
+        pairs = []
+        for r in range(args.steps):
+            for jj, f in enumerate(launches(*sets[r % N_SETS])):
+                if jj == j:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    f()
+                    b.record(stream)
+                    pairs.append((a, b))
+                else:
+                    f()
+        torch.cuda.synchronize()
+        per_b2b[name] = per[name]
+        per[name] = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
     for t, v in zip((lin.history, lin.cursor, lin.scale, lin._acc), saved):
         t.copy_(v)
     torch.cuda.synchronize()
@@ -687,6 +712,7 @@ def main():
         "gemm_tflops": gemm_tflops,
         "cast_gbps": cast_gbps,
         "kernel_ms": {n: round(v, 4) for n, v in avg.items()},
+        "gemm_ms_back_to_back": {n: round(v, 4) for n, v in per_b2b.items()},
         "step_ms_distribution": step_dist,
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "sum_of_kernel_ms": round(sum(avg.values()), 4),
