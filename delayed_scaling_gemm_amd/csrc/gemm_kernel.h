@@ -1076,7 +1076,34 @@ __global__ __launch_bounds__(256 * KS, 1) void gemm_kernel(GemmArgs p) {
     }
     // LOADS: the stage issues the direct loads of stage kt + 2, one after each
     // of its second step's MFMAs (a separate instantiation for the last two
-    // stages, so that no branch separates the loads from those MFMAs)
+    // stages, so that no branch separates the loads from those MFMAs).
+    // 256 x 256 tiles with direct loads fix the issue order further: step 1's
+    // LDS reads go between step 0's MFMAs, and the next stage's reads and this
+    // stage's loads between step 1's.  Left to the scheduler, the reads of step 1
+    // followed all of step 0's MFMAs; with 16 or more LDS reads in flight the
+    // in-order LDS counter cannot wait for the older ones alone, so the first
+    // MFMA of the next step waited for all of them (+4-10% on the three layouts).
+    constexpr bool kFixOrder = DIRECT && BM == 256 && BN == 256;
+    constexpr int kMf = FM * FN;  // MFMAs per step
+    constexpr int kDs = (A_MN_LDS ? 4 : 2) * FM + (B_MN_LDS ? 4 : 2) * FN;  // LDS reads per step
+    static_assert(!kFixOrder || (kDs >= kMf && kDs <= 2 * kMf && kDs % (kMf / 2) == 0 &&
+                                 (kIssuesA + kIssuesB) % (kMf / 2) == 0),
+                  "issue pattern for 256 x 256 tiles");
+    // one MFMA followed by two or one LDS reads, kDs reads over kMf MFMAs
+    auto order_reads = [&]() {
+      if constexpr (kFixOrder) {
+#pragma unroll
+        for (int k = 0; k < kDs - kMf; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        }
+#pragma unroll
+        for (int k = 0; k < 2 * kMf - kDs; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+    };
     auto stage = [&](int kt, auto more_tag, auto loads_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
       constexpr bool LOADS = DIRECT && decltype(loads_tag)::value;
@@ -1098,6 +1125,10 @@ __global__ __launch_bounds__(256 * KS, 1) void gemm_kernel(GemmArgs p) {
         lb.store(lds_b[cur ^ 1], tid);
       }
       mma(ra[0], rb[0], 0);
+      if constexpr (kFixOrder) {
+        order_reads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if constexpr (MORE) {
         if constexpr (DIRECT) vmem_wait_all();
         __syncthreads();
@@ -1105,12 +1136,27 @@ __global__ __launch_bounds__(256 * KS, 1) void gemm_kernel(GemmArgs p) {
         if constexpr (LOADS) issue_direct(kt + 2, cur);
       }
       mma(ra[1], rb[1], 1);
-      if constexpr (LOADS) {
+      if constexpr (LOADS && kFixOrder) {
+        // the next stage's reads over the first half of the MFMAs, the loads
+        // over the second half
+#pragma unroll
+        for (int k = 0; k < kMf / 2; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, kDs / (kMf / 2), 0);
+        }
+#pragma unroll
+        for (int k = 0; k < kMf / 2; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, (kIssuesA + kIssuesB) / (kMf / 2), 0);  // VMEM read
+        }
+      } else if constexpr (LOADS) {
 #pragma unroll
         for (int k = 0; k < kIssuesA + kIssuesB; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
         }
+      } else if constexpr (MORE) {
+        order_reads();
       }
     };
     int kt = 0;
