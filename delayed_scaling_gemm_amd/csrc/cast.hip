@@ -72,14 +72,18 @@ struct CastArgs {
 // fewer-than-one-piece elements, go element by element.
 //
 // Workgroup shape (threads T, groups per thread G), measured on MI355X over
-// BF16 casts: 1024 x 4 (64 Ki elements per workgroup) is best on tensors of
-// tens of millions of elements, where it makes exactly two rounds of two
-// resident workgroups per CU on a 4096 x 16384 tensor; 256 x 8 (32 Ki) is 5-7%
-// faster on 2^30 elements, where the rounds are many and more, smaller
-// workgroups keep more loads in flight per CU (6.1-6.2 against 5.8-5.9 TB/s).
-// The counting cast (STATS) and the amax alone stay at 1024 x 4 at every size:
-// with their extra registers 256 x 8 measured 13% and 3% slower there.
+// BF16 casts to E4M3 (a sweep of 12 shapes): up to 2^28 elements small
+// workgroups win, 256 x 2 (8 Ki elements) best: 2^22 elements 8.1 -> 4.5 us,
+// 2^24 11.7 -> 11.4 us, 2^26 38 -> 34 us (5.3 -> 5.9 TB/s), 2^27 71 -> 65 us
+// (5.6 -> 6.2 TB/s) against the 1024 x 4 (64 Ki) shape the casts used before;
+// many workgroups leave only a short tail.  From 2^28 on 256 x 8 (32 Ki) and
+// 256 x 2 are equal (5.9-6.2 TB/s) and 256 x 8 is kept.  Tensors of at most
+// 64 Ki elements take one 1024 x 4 workgroup (the batched casts of small
+// tensors rely on it).  The counting cast (STATS) and the amax alone stay at
+// 1024 x 4 at every size: with their extra registers 256 x 8 measured 13% and
+// 3% slower there.
 constexpr int64_t kCastLargeElems = int64_t(1) << 28;  // from here on: 256 x 8
+constexpr int64_t kCastMidElems = int64_t(1) << 16;    // above this: 256 x 2
 
 template <bool BF16, int T, int G>
 struct CastGroups {
@@ -354,6 +358,8 @@ static hipError_t launch_cast_t(const CastArgs& a, int64_t batch, hipStream_t st
   if constexpr (WRITE_Q && !STATS) {
     if (a.n >= kCastLargeElems)
       return launch_cast_shape<BF16, FMT, WRITE_Q, STATS, 256, 8>(a, batch, stream);
+    if (a.n > kCastMidElems)
+      return launch_cast_shape<BF16, FMT, WRITE_Q, STATS, 256, 2>(a, batch, stream);
   }
   return launch_cast_shape<BF16, FMT, WRITE_Q, STATS, 1024, 4>(a, batch, stream);
 }
@@ -389,7 +395,7 @@ hipError_t launch_cast(const void* x, bool bf16, int64_t batch, int64_t n, int64
 // scale, and the prologue kernel (with its launch gap) is not needed.  Larger
 // tensors take the prologue and the atomic reductions.
 constexpr int64_t kOneBlockElems = 1024 * 4 * 16;
-static_assert(kOneBlockElems < kCastLargeElems, "such tensors take the 1024 x 4 shape");
+static_assert(kOneBlockElems <= kCastMidElems, "such tensors take the 1024 x 4 shape");
 
 hipError_t launch_cast_batched(const void* x, bool bf16, int64_t batch, int64_t n,
                                int64_t stride_x, int fmt, const float* scale, uint8_t* q,
