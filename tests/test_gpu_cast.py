@@ -95,11 +95,14 @@ def test_midpoints_and_neighbours(fmt):
     assert np.array_equal(q, ofp8.encode(pts, fmt))
 
 
-# Workgroups own 65536 elements in 16-byte pieces (8 BF16 / 4 FP32 elements) that
-# form 16-element groups with partners 1024 pieces apart: the larger sizes end in
-# a partial workgroup whose last pieces lack partners, plus a sub-piece tail.
-@pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 255, 4099, 65536 + 9, 65536 + 8 * 1024 + 5,
-                               3 * 65536 + 12345, (1 << 20) + 3])
+# A tensor of at most 65536 elements is one workgroup of 1024 threads whose 16-byte
+# pieces (8 BF16 / 4 FP32 elements) form 16-element groups with partners 1024
+# pieces apart; larger tensors take workgroups of 256 threads and 8192 elements,
+# partners 256 pieces apart.  The sizes cover both shapes and the switch between
+# them (65536, 65537), partial last workgroups whose last pieces lack partners
+# (3 * 65536 + 12345), and sub-piece tails.
+@pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 255, 4099, 65536, 65537, 65536 + 9,
+                               65536 + 8 * 1024 + 5, 3 * 65536 + 12345, (1 << 20) + 3])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_small_and_ragged_sizes(n, bf16):
     rng = np.random.default_rng(n)
@@ -264,12 +267,14 @@ def test_stress_tensor_full_size(fmt):
 
 
 @pytest.mark.parametrize("bf16", [True, False])
-def test_large_ragged_cast(bf16):
-    """A tensor past the size where the cast switches to its large-tensor
-    workgroup shape, with a ragged tail (not a whole number of pieces or
-    workgroups): amax and saturation count exact over everything, bytes exact on
-    a sample that includes both ends and every saturating element."""
-    n = (1 << 28) + 12345 + (3 if bf16 else 1)
+@pytest.mark.parametrize("base", [(1 << 28) - 4110, (1 << 28) + 12345])
+def test_large_ragged_cast(bf16, base):
+    """Tensors just below and past 2^28 elements, where the cast switches from
+    workgroups of 8192 elements to its large-tensor shape (32768), with a ragged
+    tail (not a whole number of pieces or workgroups): amax and saturation count
+    exact over everything, bytes exact on a sample that includes both ends and
+    every saturating element."""
+    n = base + (3 if bf16 else 1)
     print(f"[large ragged cast] bf16={bf16} n={n}", flush=True)
     x = workloads.normal(n, 4242, 1.0)
     x[np.random.default_rng(5).choice(n, 997, replace=False)] = 1000.0  # saturate at s = 1
@@ -298,10 +303,9 @@ def test_large_ragged_cast(bf16):
 @pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("n", [(1 << 22) + 12345, (1 << 23) + 7])
 def test_large_ragged_tensor_every_byte(fmt, bf16, n):
-    """Single tensors from 2^22 elements on take the persistent cast (chunks walked
-    by about two workgroups per CU): every byte, the amax and the saturation count
-    of a ragged length (partial last chunk, partial groups, a tail below one
-    16-byte piece) against the oracle."""
+    """Tensors of 2^22 and 2^23 elements (many workgroups of 8192 elements): every
+    byte, the amax and the saturation count of a ragged length (partial last
+    workgroup, partial groups, a tail below one 16-byte piece) against the oracle."""
     rng = np.random.default_rng(n + 2 * fmt + int(bf16))
     x32 = (rng.standard_normal(n) * 3.0).astype(np.float32)
     x32[rng.choice(n, 101, replace=False)] = 7.0e4  # saturate both formats
