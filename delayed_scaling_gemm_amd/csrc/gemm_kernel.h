@@ -744,27 +744,43 @@ __global__ __launch_bounds__(256 * KS, 1) void gemm_kernel(GemmArgs p) {
   const int tr_i = lane & 15;
   const int tr_row = 16 * ((lane >> 4) & 1) + 8 * (tr_i & 1);  // row offset in a 32-row block
   const int tr_k = 64 * (lane >> 5) + (tr_i >> 1);              // + 16 u + 8 h
-  auto read_mn = [&](const uint8_t* tile, auto rows_tag, int r0, int u) {
-    constexpr int R = decltype(rows_tag)::value;
-    const u32x2 lo = ds_read_tr8(tile + mn_off<R>(tr_k + 16 * u, r0 + tr_row));
-    const u32x2 hi = ds_read_tr8(tile + mn_off<R>(tr_k + 16 * u + 8, r0 + tr_row));
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  // Byte offsets, within a stage buffer, of this lane's reads of unit u of each
+  // 32-row block: the 16-byte chunk fc + u of its row (K-major tiles, h = 0) or
+  // the two 8-byte transposing reads h (MN-major tiles).  They do not change
+  // from stage to stage, so a read adds only its buffer's base (recomputed per
+  // read, the address arithmetic cost ~1% of the exact GEMMs' time).
+  int offa[4][FM][2], offb[4][FN][2];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        offa[u][i][h] = A_MN_LDS ? mn_off<BM>(tr_k + 16 * u + 8 * h, wm * WTM + i * 32 + tr_row)
+                                 : lds_off(wm * WTM + i * 32 + fr, fc + u);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        offb[u][j][h] = B_MN_LDS ? mn_off<BN>(tr_k + 16 * u + 8 * h, wn * WTN + j * 32 + tr_row)
+                                 : lds_off(wn * WTN + j * 32 + fr, fc + u);
+    }
+  }
+  // unit u of a block: one 16-byte read, or two transposing 8-byte reads
+  auto read_frag = [&](const uint8_t* tile, const int (&off)[2], auto mn_tag) {
+    if constexpr (decltype(mn_tag)::value) {
+      const u32x2 lo = ds_read_tr8(tile + off[0]);
+      const u32x2 hi = ds_read_tr8(tile + off[1]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+      return *reinterpret_cast<const u32x4*>(tile + off[0]);
+    }
   };
   auto read_unit = [&](int buf, int u, u32x4 (&xa)[FM], u32x4 (&xb)[FN]) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (B_MN_LDS)
-        xb[j] = read_mn(lds_b[buf], std::integral_constant<int, BN>{}, wn * WTN + j * 32, u);
-      else
-        xb[j] = *reinterpret_cast<const u32x4*>(lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, fc + u));
-    }
+    for (int j = 0; j < FN; ++j)
+      xb[j] = read_frag(lds_b[buf], offb[u][j], std::integral_constant<bool, B_MN_LDS>{});
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if constexpr (A_MN_LDS)
-        xa[i] = read_mn(lds_a[buf], std::integral_constant<int, BM>{}, wm * WTM + i * 32, u);
-      else
-        xa[i] = *reinterpret_cast<const u32x4*>(lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, fc + u));
-    }
+    for (int i = 0; i < FM; ++i)
+      xa[i] = read_frag(lds_a[buf], offa[u][i], std::integral_constant<bool, A_MN_LDS>{});
   };
 
   // DIRECT: stages are loaded straight into LDS two stages ahead: stage k + 2
@@ -976,43 +992,31 @@ __global__ __launch_bounds__(256 * KS, 1) void gemm_kernel(GemmArgs p) {
   } else {
     u32x4 ra[2][FM][2], rb[2][FN][2];  // two chunks per step, by step parity
     // Step s of a stage takes, per lane, 32 consecutive K values of its row:
-    // k = 64 (l / 32) + 32 s + [0, 32) (MX: the chunks described at `mma`).
-    // K-major tiles give them as two 16-byte chunks; MN-major tiles (direct loads
-    // of MN-contiguous operands) as four transposing 8-byte reads.
-    auto read_mn32 = [&](const uint8_t* tile, auto rows_tag, int r0, int s, u32x4 (&x)[2]) {
-      constexpr int R = decltype(rows_tag)::value;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x2 lo = ds_read_tr8(tile + mn_off<R>(tr_k + 32 * s + 16 * h, r0 + tr_row));
-        const u32x2 hi = ds_read_tr8(tile + mn_off<R>(tr_k + 32 * s + 16 * h + 8, r0 + tr_row));
-        x[h] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-    };
+    // k = 64 (l / 32) + 32 s + [0, 32), i.e. units 2 s and 2 s + 1 of the exact
+    // path's reads (MX: the chunks described at `mma`).
     auto read_step = [&](int buf, int s, u32x4 (&xa)[FM][2], u32x4 (&xb)[FN][2]) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (B_MN_LDS) {
-          read_mn32(lds_b[buf], std::integral_constant<int, BN>{}, wn * WTN + j * 32, s, xb[j]);
-        } else {
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+          if constexpr (MX)
             xb[j][t] = *reinterpret_cast<const u32x4*>(
-                lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, MX ? 4 * s + 2 * t + (lane >> 5)
-                                                                : fc + 2 * s + t));
+                lds_b[buf] + lds_off(wn * WTN + j * 32 + fr, 4 * s + 2 * t + (lane >> 5)));
+          else
+            xb[j][t] = read_frag(lds_b[buf], offb[2 * s + t][j],
+                                 std::integral_constant<bool, B_MN_LDS>{});
         }
-      }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        if constexpr (A_MN_LDS) {
-          read_mn32(lds_a[buf], std::integral_constant<int, BM>{}, wm * WTM + i * 32, s, xa[i]);
-        } else {
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+          if constexpr (MX)
             xa[i][t] = *reinterpret_cast<const u32x4*>(
-                lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, MX ? 4 * s + 2 * t + (lane >> 5)
-                                                                : fc + 2 * s + t));
+                lds_a[buf] + lds_off(wm * WTM + i * 32 + fr, 4 * s + 2 * t + (lane >> 5)));
+          else
+            xa[i][t] = read_frag(lds_a[buf], offa[2 * s + t][i],
+                                 std::integral_constant<bool, A_MN_LDS>{});
         }
-      }
     };
     // MX: this lane's E8M0 scale dwords (the 4 blocks of a stage per row), loaded
     // a stage ahead.  The block-scaled instruction (probed on gfx950) scales
